@@ -1,0 +1,539 @@
+// Causal grouped-query attention for gfx950.
+//
+// Definition (LLaMA notes, section 3, Attention.forward; causal mask with cache
+// offset from "灵哥讲llama3(中)", Transformer forward): for query head h at
+// sequence index s, kv head j = h / n_rep, keys t <= start_pos + s:
+//     o = sum_t softmax_t(q . k_t / sqrt(d)) v_t.
+// The kernels compute it as an exact rearrangement: scores in fp32, a running
+// (max, sum) online softmax in the log2 domain, probabilities rounded to bf16
+// only as the operand of the P.V contraction.
+//
+// Prefill (bf16): one workgroup owns 128 query rows = G heads of one kv group
+// x 128/G positions, so each K/V tile is staged in LDS once and used by all G
+// heads (GQA sharing).  Key tiles entirely above the causal diagonal of the
+// block are never loaded.  S^T = K.Q^T and O^T = V^T.P^T on
+// v_mfma_f32_32x32x16_bf16 put one query row per lane column, so the row
+// max/sum need one cross-half exchange only, and the probabilities feed the
+// second MFMA straight from registers (keys are permuted in the V^T tile to
+// match the accumulator layout).
+//
+// Decode (bf16): split-K over keys.  Each wave streams chunks of 32 keys from
+// HBM (K straight into MFMA operand registers, V through a wave-private
+// transposed LDS tile), keeps its own online-softmax state for all n_rep heads
+// of the kv group (padded to 16 on v_mfma_f32_16x16x32_bf16), the four waves
+// merge in LDS and each split writes (max, sum, o) partials that a second
+// kernel combines with log-sum-exp weights.
+//
+// f32: one wavefront per (b, s, h) with scalar online softmax (small shapes).
+#include "attention.hpp"
+
+#include <math.h>
+
+namespace llama {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ------------------------------------------------------------------ KV append
+template <typename T>
+__global__ void kv_append_kernel(const T* __restrict__ xk, const T* __restrict__ xv, T* __restrict__ ck,
+                                 T* __restrict__ cv, AttnShape sh) {
+  const int row = sh.n_kv_heads * sh.head_dim;  // elements per (b, position)
+  const int64_t total4 = (int64_t)sh.bsz * sh.seqlen * row / 4;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total4;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    int64_t e = i * 4;
+    int64_t bs = e / row;
+    int c = (int)(e - bs * row);
+    int b = (int)(bs / sh.seqlen), s = (int)(bs - (int64_t)b * sh.seqlen);
+    int64_t dst = ((int64_t)b * sh.max_seq + sh.start_pos + s) * row + c;
+    store4(ck + dst, load4(xk + e));
+    store4(cv + dst, load4(xv + e));
+  }
+}
+
+// ------------------------------------------------------------------ simple (f32)
+template <typename T>
+__global__ void __launch_bounds__(256) attn_simple(const T* __restrict__ q, const T* __restrict__ ck,
+                                                   const T* __restrict__ cv, T* __restrict__ out,
+                                                   AttnShape sh, float scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int H = sh.n_heads, HD = sh.head_dim, S = sh.seqlen;
+  if (wid >= (int64_t)sh.bsz * S * H) return;
+  const int h = (int)(wid % H);
+  const int64_t bs = wid / H;
+  const int b = (int)(bs / S), s = (int)(bs % S);
+  const int n_rep = H / sh.n_kv_heads;
+  const int j = h / n_rep;
+  const T* qr = q + bs * (int64_t)H * HD + (int64_t)h * HD;
+  const bool has0 = lane < HD, has1 = lane + 64 < HD;
+  const float q0 = has0 ? to_f(qr[lane]) : 0.f;
+  const float q1 = has1 ? to_f(qr[lane + 64]) : 0.f;
+  const int64_t stride = (int64_t)sh.n_kv_heads * HD;
+  const T* kb = ck + ((int64_t)b * sh.max_seq * sh.n_kv_heads + j) * HD;
+  const T* vb = cv + ((int64_t)b * sh.max_seq * sh.n_kv_heads + j) * HD;
+  const int kend = sh.start_pos + s + 1;
+  float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int t = 0; t < kend; ++t) {
+    const T* kr = kb + (int64_t)t * stride;
+    float part = (has0 ? q0 * to_f(kr[lane]) : 0.f) + (has1 ? q1 * to_f(kr[lane + 64]) : 0.f);
+    float sc = wave_sum(part) * scale;
+    float mn = fmaxf(m, sc);
+    float a = expf(m - mn), p = expf(sc - mn);
+    const T* vr = vb + (int64_t)t * stride;
+    l = l * a + p;
+    o0 = o0 * a + (has0 ? p * to_f(vr[lane]) : 0.f);
+    o1 = o1 * a + (has1 ? p * to_f(vr[lane + 64]) : 0.f);
+    m = mn;
+  }
+  T* orow = out + bs * (int64_t)H * HD + (int64_t)h * HD;
+  if (has0) orow[lane] = from_f<T>(o0 / l);
+  if (has1) orow[lane + 64] = from_f<T>(o1 / l);
+}
+
+// ------------------------------------------------------------------ prefill (bf16 MFMA)
+template <int HD>
+__global__ void __launch_bounds__(256, 2)
+attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const bf16* __restrict__ cv,
+                  bf16* __restrict__ out, AttnShape sh, int G, float scale_log2) {
+  constexpr int BKV = 64;
+  constexpr int CHK = HD / 8;                 // 16-byte chunks per K row
+  constexpr int KL = BKV * CHK / 256;         // K chunks per thread per tile
+  constexpr int VT = 16 * CHK;                // V transpose tasks (4 keys x 8 d each)
+  static_assert(HD == 64 || HD == 128, "head_dim");
+  __shared__ bf16x8 Ks[2][BKV * CHK];         // [key][chunk ^ (key & 7)]
+  __shared__ bf16x8 Vt[2][HD * (BKV / 8)];    // [d][key chunk ^ (d & 7)], keys permuted
+
+  const int H = sh.n_heads, Hkv = sh.n_kv_heads, S = sh.seqlen, p0 = sh.start_pos;
+  const int n_rep = H / Hkv;
+  const int BQ = 128 / G;
+  const int hgroups = H / G;
+  const int qblocks = (S + BQ - 1) / BQ;
+  const int per = hgroups * sh.bsz;
+  const int qb = qblocks - 1 - (int)(blockIdx.x / per);   // heavy (late) query blocks first
+  const int rest = blockIdx.x % per;
+  const int hg = rest % hgroups, b = rest / hgroups;
+  const int h0 = hg * G;
+  const int j = h0 / n_rep;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int R = wave * 32 + lrow;
+  const int s = qb * BQ + R % BQ;
+  const int h = h0 + R / BQ;
+  const bool row_valid = s < S;
+  const int s_c = row_valid ? s : S - 1;
+  const int qpos = p0 + s;
+
+  bf16x8 qf[HD / 16];
+  {
+    const bf16* qr = q + (((int64_t)b * S + s_c) * H + h) * HD;
+#pragma unroll
+    for (int kk = 0; kk < HD / 16; ++kk) qf[kk] = *(const bf16x8*)(qr + (kk * 2 + lhalf) * 8);
+  }
+
+  const int s_hi = min(S - 1, qb * BQ + BQ - 1);
+  const int kend = p0 + s_hi + 1;
+  const int ntiles = (kend + BKV - 1) / BKV;
+  const int64_t stride = (int64_t)Hkv * HD;
+  const bf16* kbase = ck + ((int64_t)b * sh.max_seq * Hkv + j) * HD;
+  const bf16* vbase = cv + ((int64_t)b * sh.max_seq * Hkv + j) * HD;
+
+  bf16x8 kreg[KL], vreg[4];
+  auto gload = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      int key = t0 + tid / CHK + i * (256 / CHK);
+      int c = tid % CHK;
+      kreg[i] = key < kend ? *(const bf16x8*)(kbase + key * stride + c * 8) : bf16x8{};
+    }
+    if (tid < VT) {
+      int kg = tid / CHK, c = tid % CHK;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        int key = t0 + kg * 4 + e;
+        vreg[e] = key < kend ? *(const bf16x8*)(vbase + key * stride + c * 8) : bf16x8{};
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      int key = tid / CHK + i * (256 / CHK);
+      int c = tid % CHK;
+      Ks[buf][key * CHK + (c ^ (key & 7))] = kreg[i];
+    }
+    if (tid < VT) {
+      int kg = tid / CHK, dc = tid % CHK;
+      int g4 = kg & 3;
+      int g4p = (g4 == 1) ? 2 : (g4 == 2 ? 1 : g4);   // swap the middle 4-key groups
+      int pos = (kg >> 2) * 16 + g4p * 4;
+      int pc = pos >> 3, off = pos & 7;
+#pragma unroll
+      for (int e8 = 0; e8 < 8; ++e8) {
+        int d = dc * 8 + e8;
+        bf16x4 v4 = {vreg[0][e8], vreg[1][e8], vreg[2][e8], vreg[3][e8]};
+        bf16* rowp = (bf16*)&Vt[buf][d * 8 + (pc ^ (d & 7))];
+        *(bf16x4*)(rowp + off) = v4;
+      }
+    }
+  };
+
+  f32x16 oacc[HD / 32];
+#pragma unroll
+  for (int i = 0; i < HD / 32; ++i) oacc[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const int t0 = it * BKV;
+    if (it + 1 < ntiles) gload(t0 + BKV);
+
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key = kt * 32 + lrow;
+#pragma unroll
+      for (int kk = 0; kk < HD / 16; ++kk) {
+        const int c = kk * 2 + lhalf;
+        bf16x8 kf = Ks[buf][key * CHK + (c ^ (key & 7))];
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[kt], 0, 0, 0);
+      }
+    }
+    // scale, causal mask, row max (lane holds 32 of the row's 64 keys; lane^32 the rest)
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        int t = t0 + kt * 32 + (v >> 2) * 8 + lhalf * 4 + (v & 3);
+        float x = sacc[kt][v] * scale_log2;
+        x = (t > qpos) ? -INFINITY : x;
+        sacc[kt][v] = x;
+        mloc = fmaxf(mloc, x);
+      }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float m_new = fmaxf(m_run, mloc);
+    const float alpha = exp2f(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float p = exp2f(sacc[kt][v] - m_new);
+        sacc[kt][v] = p;
+        psum += p;
+      }
+    psum += __shfl_xor(psum, 32, 64);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < HD / 32; ++dt) oacc[dt] *= alpha;
+
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        bf16x8 pf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[e] = (bf16)sacc[kt][h2 * 8 + e];
+        const int pc = kt * 4 + h2 * 2 + lhalf;
+#pragma unroll
+        for (int dt = 0; dt < HD / 32; ++dt) {
+          const int d = dt * 32 + lrow;
+          bf16x8 vf = Vt[buf][d * 8 + (pc ^ (d & 7))];
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[dt], 0, 0, 0);
+        }
+      }
+    if (it + 1 < ntiles) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!row_valid) return;
+  const float inv = 1.0f / l_run;
+  bf16* orow = out + (((int64_t)b * S + s) * H + h) * HD;
+#pragma unroll
+  for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4 v = {oacc[dt][g * 4], oacc[dt][g * 4 + 1], oacc[dt][g * 4 + 2], oacc[dt][g * 4 + 3]};
+      store4(orow + dt * 32 + g * 8 + lhalf * 4, v * inv);
+    }
+}
+
+// ------------------------------------------------------------------ decode (bf16 MFMA, split-K)
+template <int HD>
+__global__ void __launch_bounds__(256)
+attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const bf16* __restrict__ cv,
+                 bf16* __restrict__ out, float* __restrict__ partial, AttnShape sh, int nsplit, int L,
+                 float scale_log2) {
+  constexpr int CH = HD / 8;
+  static_assert(HD == 64 || HD == 128, "head_dim");
+  __shared__ bf16x8 Vt[4][HD * 4];          // per wave: [d][4 chunks of 8 permuted keys]
+  __shared__ float mrg_m[4][16], mrg_l[4][16];
+
+  const int H = sh.n_heads, Hkv = sh.n_kv_heads;
+  const int n_rep = H / Hkv;
+  const int hgs = (n_rep + 15) / 16;
+  const int z = blockIdx.x;
+  const int j = blockIdx.y / hgs, hg = blockIdx.y % hgs;
+  const int b = blockIdx.z;
+  const int T = sh.start_pos + 1;
+  const int t_begin = z * L, t_end = min(T, t_begin + L);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int hl = hg * 16 + l16;               // head within the kv group
+  const bool hvalid = hl < n_rep;
+  const int h = j * n_rep + (hvalid ? hl : 0);
+
+  bf16x8 qf[HD / 32];
+  {
+    const bf16* qr = q + ((int64_t)b * H + h) * HD;
+#pragma unroll
+    for (int kk = 0; kk < HD / 32; ++kk)
+      qf[kk] = hvalid ? *(const bf16x8*)(qr + (kk * 4 + g) * 8) : bf16x8{};
+  }
+  const int64_t stride = (int64_t)Hkv * HD;
+  const bf16* kbase = ck + ((int64_t)b * sh.max_seq * Hkv + j) * HD;
+  const bf16* vbase = cv + ((int64_t)b * sh.max_seq * Hkv + j) * HD;
+
+  f32x4 oacc[HD / 16];
+#pragma unroll
+  for (int i = 0; i < HD / 16; ++i) oacc[i] = f32x4{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const bool vtask = lane < 4 * CH;
+  const int vg = lane / CH, vdc = lane % CH;
+
+  for (int c0 = t_begin + wave * 32; c0 < t_end; c0 += 128) {
+    bf16x8 kf[2][HD / 32];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key = c0 + kt * 16 + l16;
+#pragma unroll
+      for (int kk = 0; kk < HD / 32; ++kk)
+        kf[kt][kk] = key < t_end ? *(const bf16x8*)(kbase + key * stride + (kk * 4 + g) * 8) : bf16x8{};
+    }
+    bf16x8 vk[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int key = c0 + (e < 4 ? vg * 4 + e : 16 + vg * 4 + (e - 4));
+      vk[e] = (vtask && key < t_end) ? *(const bf16x8*)(vbase + key * stride + vdc * 8) : bf16x8{};
+    }
+    if (vtask) {
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        const int d = vdc * 8 + dd;
+        bf16x8 w = {vk[0][dd], vk[1][dd], vk[2][dd], vk[3][dd], vk[4][dd], vk[5][dd], vk[6][dd], vk[7][dd]};
+        Vt[wave][d * 4 + (vg ^ ((d >> 1) & 3))] = w;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    f32x4 sacc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int kk = 0; kk < HD / 32; ++kk)
+        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt][kk], qf[kk], sacc[kt], 0, 0, 0);
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int key = c0 + kt * 16 + g * 4 + v;
+        float x = key < t_end ? sacc[kt][v] * scale_log2 : -INFINITY;
+        sacc[kt][v] = x;
+        mloc = fmaxf(mloc, x);
+      }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float m_new = fmaxf(m_run, mloc);
+    const float alpha = exp2f(m_run - m_new);
+    float psum = 0.f;
+    bf16x8 pf;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float p = exp2f(sacc[kt][v] - m_new);
+        psum += p;
+        pf[kt * 4 + v] = (bf16)p;
+      }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < HD / 16; ++dt) {
+      const int d = dt * 16 + l16;
+      bf16x8 vf = Vt[wave][d * 4 + (g ^ ((d >> 1) & 3))];
+      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[dt] * alpha, 0, 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // merge the four waves' (max, sum, o) in LDS
+  __syncthreads();
+  float* obuf = (float*)&Vt[0][0];            // [4 waves][16 heads][HD] floats
+  if (g == 0) {
+    mrg_m[wave][l16] = m_run;
+    mrg_l[wave][l16] = l_run;
+  }
+#pragma unroll
+  for (int dt = 0; dt < HD / 16; ++dt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) obuf[(wave * 16 + l16) * HD + dt * 16 + g * 4 + v] = oacc[dt][v];
+  __syncthreads();
+
+  const int hh = tid >> 4;                    // head slot 0..15
+  const int d0 = (tid & 15) * (HD / 16);
+  const int hl2 = hg * 16 + hh;
+  if (hl2 >= n_rep) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, mrg_m[w][hh]);
+  float wt[4], Ls = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    wt[w] = mrg_m[w][hh] == -INFINITY ? 0.f : exp2f(mrg_m[w][hh] - M);
+    Ls += wt[w] * mrg_l[w][hh];
+  }
+  float o[HD / 16];
+#pragma unroll
+  for (int k = 0; k < HD / 16; ++k) {
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc += wt[w] * obuf[(w * 16 + hh) * HD + d0 + k];
+    o[k] = acc;
+  }
+  const int hq = j * n_rep + hl2;
+  if (nsplit == 1) {
+    bf16* orow = out + ((int64_t)b * H + hq) * HD + d0;
+    const float inv = 1.0f / Ls;
+#pragma unroll
+    for (int k = 0; k < HD / 16; k += 4) store4(orow + k, f32x4{o[k], o[k + 1], o[k + 2], o[k + 3]} * inv);
+  } else {
+    float* p = partial + (((int64_t)b * H + hq) * nsplit + z) * (HD + 2);
+#pragma unroll
+    for (int k = 0; k < HD / 16; ++k) p[d0 + k] = o[k];
+    if ((tid & 15) == 0) {
+      p[HD] = M;
+      p[HD + 1] = Ls;
+    }
+  }
+}
+
+template <typename T>
+__global__ void attn_decode_combine(const float* __restrict__ partial, T* __restrict__ out, int nsplit,
+                                    int HD) {
+  const int64_t bh = blockIdx.x;
+  const int d = threadIdx.x;
+  const float* base = partial + bh * nsplit * (HD + 2);
+  float M = -INFINITY;
+  for (int z = 0; z < nsplit; ++z) M = fmaxf(M, base[z * (HD + 2) + HD]);
+  float acc = 0.f, Ls = 0.f;
+  for (int z = 0; z < nsplit; ++z) {
+    const float* p = base + z * (HD + 2);
+    float w = p[HD] == -INFINITY ? 0.f : exp2f(p[HD] - M);
+    Ls += w * p[HD + 1];
+    acc += w * p[d];
+  }
+  out[bh * HD + d] = from_f<T>(acc / Ls);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ host launchers
+template <typename T>
+hipError_t kv_append(const T* xk, const T* xv, T* cache_k, T* cache_v, const AttnShape& sh,
+                     hipStream_t st) {
+  int64_t total4 = (int64_t)sh.bsz * sh.seqlen * sh.n_kv_heads * sh.head_dim / 4;
+  if (total4 == 0) return hipSuccess;
+  int64_t nb = (total4 + 255) / 256;
+  int blocks = (int)(nb < 8192 ? nb : 8192);
+  kv_append_kernel<T><<<blocks, 256, 0, st>>>(xk, xv, cache_k, cache_v, sh);
+  return hipGetLastError();
+}
+
+static int prefill_group(int n_rep) {
+  int g = 1;
+  while (g < 8 && n_rep % (g * 2) == 0) g *= 2;
+  return g;
+}
+
+template <typename T>
+hipError_t attn_prefill(const T* q, const T* cache_k, const T* cache_v, T* out, const AttnShape& sh,
+                        hipStream_t st) {
+  const float scale = 1.0f / sqrtf((float)sh.head_dim);
+  if constexpr (sizeof(T) == 2) {
+    const int G = prefill_group(sh.n_heads / sh.n_kv_heads);
+    const int BQ = 128 / G;
+    const int64_t blocks = (int64_t)((sh.seqlen + BQ - 1) / BQ) * (sh.n_heads / G) * sh.bsz;
+    if (sh.head_dim == 128)
+      attn_prefill_mfma<128><<<(unsigned)blocks, 256, 0, st>>>(q, cache_k, cache_v, out, sh, G, scale * kLog2e);
+    else
+      attn_prefill_mfma<64><<<(unsigned)blocks, 256, 0, st>>>(q, cache_k, cache_v, out, sh, G, scale * kLog2e);
+  } else {
+    const int64_t waves = (int64_t)sh.bsz * sh.seqlen * sh.n_heads;
+    attn_simple<T><<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(q, cache_k, cache_v, out, sh, scale);
+  }
+  return hipGetLastError();
+}
+
+int attn_decode_splits(int bsz, int n_heads, int n_kv_heads, int T) {
+  const int n_rep = n_heads / n_kv_heads;
+  const int units = bsz * n_kv_heads * ((n_rep + 15) / 16);
+  int ns = (1024 + units - 1) / units;
+  ns = max(1, min(ns, (T + 127) / 128));
+  int L = (T + ns - 1) / ns;
+  L = (L + 31) / 32 * 32;
+  return (T + L - 1) / L;
+}
+
+template <typename T>
+hipError_t attn_decode(const T* q, const T* cache_k, const T* cache_v, T* out, const AttnShape& sh,
+                       float* partial, hipStream_t st) {
+  const float scale = 1.0f / sqrtf((float)sh.head_dim);
+  if constexpr (sizeof(T) == 2) {
+    const int T_ = sh.start_pos + 1;
+    const int ns = attn_decode_splits(sh.bsz, sh.n_heads, sh.n_kv_heads, T_);
+    int L = (T_ + ns - 1) / ns;
+    L = (L + 31) / 32 * 32;
+    const int n_rep = sh.n_heads / sh.n_kv_heads;
+    dim3 grid(ns, sh.n_kv_heads * ((n_rep + 15) / 16), sh.bsz);
+    if (sh.head_dim == 128)
+      attn_decode_mfma<128><<<grid, 256, 0, st>>>(q, cache_k, cache_v, out, partial, sh, ns, L, scale * kLog2e);
+    else
+      attn_decode_mfma<64><<<grid, 256, 0, st>>>(q, cache_k, cache_v, out, partial, sh, ns, L, scale * kLog2e);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || ns == 1) return e;
+    attn_decode_combine<T><<<sh.bsz * sh.n_heads, sh.head_dim, 0, st>>>(partial, out, ns, sh.head_dim);
+  } else {
+    const int64_t waves = (int64_t)sh.bsz * sh.n_heads;
+    attn_simple<T><<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(q, cache_k, cache_v, out, sh, scale);
+  }
+  return hipGetLastError();
+}
+
+template hipError_t kv_append<bf16>(const bf16*, const bf16*, bf16*, bf16*, const AttnShape&, hipStream_t);
+template hipError_t kv_append<float>(const float*, const float*, float*, float*, const AttnShape&, hipStream_t);
+template hipError_t attn_prefill<bf16>(const bf16*, const bf16*, const bf16*, bf16*, const AttnShape&, hipStream_t);
+template hipError_t attn_prefill<float>(const float*, const float*, const float*, float*, const AttnShape&,
+                                        hipStream_t);
+template hipError_t attn_decode<bf16>(const bf16*, const bf16*, const bf16*, bf16*, const AttnShape&, float*,
+                                      hipStream_t);
+template hipError_t attn_decode<float>(const float*, const float*, const float*, float*, const AttnShape&,
+                                       float*, hipStream_t);
+
+}  // namespace llama

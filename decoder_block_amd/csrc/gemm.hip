@@ -1,0 +1,421 @@
+// Projection GEMMs C[m][n] = sum_k A[m][k] W[n][k] for gfx950.
+//
+// bf16: LDS-staged, double-buffered tiles feeding v_mfma_f32_32x32x16_bf16.
+// The weight tile is the MFMA "A" operand (rows i = n) and the activation tile
+// the "B" operand (columns j = m), so each lane's accumulators hold four
+// consecutive output columns n of one token row m: the epilogue can rotate
+// RoPE pairs and pair w1/w3 results in registers and store 8-byte vectors.
+// Both operands are K-contiguous (nn.Linear layout), which is the layout the
+// MFMA wants per lane (8 consecutive k values); tiles sit in LDS as 16-byte
+// chunks with an XOR swizzle on the chunk index to spread rows over banks.
+//
+// f32: a plain LDS-tiled FMA kernel (the fp32 workload is tiny and launch
+// bound), same epilogues.
+#include "gemm.hpp"
+
+namespace llama {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename T>
+__device__ __forceinline__ const T* weight_row(const WeightRows<T>& w, int n, int K) {
+  if (n < w.n1) return w.w0 + (int64_t)n * K;
+  if (n < w.n2) return w.w1 + (int64_t)(n - w.n1) * K;
+  return w.w2 + (int64_t)(n - w.n2) * K;
+}
+
+// Tile coordinates of a logical workgroup id: XCD-aware remap, then grouped
+// ordering (GROUP_M tile rows share their weight tiles in L2).
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int GROUP_M = 8;
+  int nb = tiles_m * tiles_n;
+  int pid = xcd_remap(blockIdx.x, nb);
+  int in_group = GROUP_M * tiles_n;
+  int gid = pid / in_group;
+  int first_m = gid * GROUP_M;
+  int gsz = min(tiles_m - first_m, GROUP_M);
+  int r = pid - gid * in_group;
+  tm = first_m + r % gsz;
+  tn = r / gsz;
+}
+
+// ------------------------------------------------------------------ bf16 MFMA kernel
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool DUAL, bool SPLIT, class Epi>
+__global__ void __launch_bounds__(kThreads)
+gemm_bf16_mfma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M, int N, int K,
+               int k_per_split, Epi epi, float* __restrict__ partial) {
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int CH = BK / 8;                 // 16-byte chunks per tile row
+  constexpr int ROWS = BM + BN;
+  constexpr int LOADS = ROWS * CH / kThreads;
+  constexpr int BN_OUT = DUAL ? BN / 2 : BN;
+  static_assert(WAVES_M * WAVES_N == 4, "four waves");
+  static_assert(TM >= 1 && TN >= 1 && (!DUAL || TN % 2 == 0), "wave tile");
+  static_assert((ROWS * CH) % kThreads == 0 && (BM * CH) % kThreads == 0, "load split");
+  static_assert(CH == 8, "swizzle assumes 8 chunks per row");
+
+  __shared__ bf16x8 smem[2][ROWS * CH];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles_n = (N + BN_OUT - 1) / BN_OUT;
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN_OUT;
+  const int kb = blockIdx.z * k_per_split;
+  const int ke = min(K, kb + k_per_split);
+  const int nk = (ke - kb + BK - 1) / BK;
+
+  // global -> register staging: chunk q = tid + i*256 of the (A rows | W rows) tile
+  const bf16* src[LOADS];
+  int row_of[LOADS], chunk_of[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    int q = tid + i * kThreads;
+    int r = q / CH, c = q % CH;
+    row_of[i] = r;
+    chunk_of[i] = c;
+    const bf16* p = nullptr;
+    if (r < BM) {
+      int m = m0 + r;
+      if (m < M) p = A + (int64_t)m * lda;
+    } else {
+      int rb = r - BM;
+      int n;
+      if (DUAL) {
+        // rows [0, BN/2) of the weight tile come from w1, [BN/2, BN) from w3
+        n = n0 + (rb < BN / 2 ? rb : rb - BN / 2);
+        if (n < N) p = (rb < BN / 2 ? w.w0 : w.w1) + (int64_t)n * K;
+      } else {
+        n = n0 + rb;
+        if (n < N) p = weight_row(w, n, K);
+      }
+    }
+    src[i] = p ? p + c * 8 : nullptr;
+  }
+
+  bf16x8 stage[LOADS];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      if (src[i] && k0 + chunk_of[i] * 8 < ke)
+        stage[i] = *(const bf16x8*)(src[i] + k0);
+      else
+        stage[i] = bf16x8{};
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      int r = row_of[i];
+      smem[buf][r * CH + (chunk_of[i] ^ (r & 7))] = stage[i];
+    }
+  };
+
+  // LDS row (within the weight tile) of this wave's MFMA tile t
+  auto wrow = [&](int t) {
+    if (DUAL) {
+      return t < TN / 2 ? wn * (WN / 2) + t * 32 : BN / 2 + wn * (WN / 2) + (t - TN / 2) * 32;
+    }
+    return wn * WN + t * 32;
+  };
+
+  f32x16 acc[TN][TM];
+#pragma unroll
+  for (int a = 0; a < TN; ++a)
+#pragma unroll
+    for (int b = 0; b < TM; ++b) acc[a][b] = f32x16{};
+
+  if (nk > 0) {
+    gload(kb);
+    sstore(0);
+  }
+  __syncthreads();
+
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload(kb + (kt + 1) * BK);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int c = kk * 2 + lhalf;
+      bf16x8 fa[TN], fb[TM];
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        int r = BM + wrow(t) + lrow;
+        fa[t] = smem[buf][r * CH + (c ^ (r & 7))];
+      }
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        int r = wm * WM + t * 32 + lrow;
+        fb[t] = smem[buf][r * CH + (c ^ (r & 7))];
+      }
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+    }
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds n = base + g*8 + lhalf*4 + {0..3} of row m = .. + lrow
+#pragma unroll
+  for (int b = 0; b < TM; ++b) {
+    const int m = m0 + wm * WM + b * 32 + lrow;
+    if (m >= M) continue;
+    if constexpr (DUAL) {
+#pragma unroll
+      for (int a = 0; a < TN / 2; ++a)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * (WN / 2) + a * 32 + g * 8 + lhalf * 4;
+          if (n >= N) continue;
+          f32x4 v1 = {acc[a][b][g * 4], acc[a][b][g * 4 + 1], acc[a][b][g * 4 + 2], acc[a][b][g * 4 + 3]};
+          const f32x16& a3 = acc[a + TN / 2][b];
+          f32x4 v3 = {a3[g * 4], a3[g * 4 + 1], a3[g * 4 + 2], a3[g * 4 + 3]};
+          if (SPLIT) {
+            float* p = partial + ((int64_t)blockIdx.z * M + m) * (2 * (int64_t)N);
+            *(f32x4*)(p + n) = v1;
+            *(f32x4*)(p + N + n) = v3;
+          } else {
+            epi(m, n, v1, v3);
+          }
+        }
+    } else {
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * WN + a * 32 + g * 8 + lhalf * 4;
+          if (n >= N) continue;
+          f32x4 v = {acc[a][b][g * 4], acc[a][b][g * 4 + 1], acc[a][b][g * 4 + 2], acc[a][b][g * 4 + 3]};
+          if (SPLIT) {
+            *(f32x4*)(partial + ((int64_t)blockIdx.z * M + m) * (int64_t)N + n) = v;
+          } else {
+            epi(m, n, v);
+          }
+        }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ fp32 FMA kernel
+// 64 x 64 output tile, BK = 16; each thread owns a 4 (m) x 4 (n) block with
+// 4 consecutive columns per row, matching the epilogue interface.
+template <bool DUAL, bool SPLIT, class Epi>
+__global__ void __launch_bounds__(kThreads)
+gemm_f32_fma(const float* __restrict__ A, int64_t lda, WeightRows<float> w, int M, int N, int K,
+             int k_per_split, Epi epi, float* __restrict__ partial) {
+  constexpr int BM = 64, BN = 64, BK = 16;
+  __shared__ float As[BK][BM + 4];
+  __shared__ float Ws[DUAL ? 2 : 1][BK][BN + 4];
+  const int tid = threadIdx.x;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kb = blockIdx.z * k_per_split, ke = min(K, kb + k_per_split);
+  const int tx = tid % 16, ty = tid / 16;  // n block tx*4, m block ty*4
+  float acc[DUAL ? 2 : 1][4][4] = {};
+  for (int k0 = kb; k0 < ke; k0 += BK) {
+    // each thread loads 4 elements of A and 4 (x2) of W
+    for (int e = tid; e < BM * BK; e += kThreads) {
+      int r = e / BK, c = e % BK;
+      int m = m0 + r, k = k0 + c;
+      As[c][r] = (m < M && k < ke) ? A[(int64_t)m * lda + k] : 0.f;
+      int n = n0 + r;
+      if (DUAL) {
+        Ws[0][c][r] = (n < N && k < ke) ? w.w0[(int64_t)n * K + k] : 0.f;
+        Ws[DUAL ? 1 : 0][c][r] = (n < N && k < ke) ? w.w1[(int64_t)n * K + k] : 0.f;
+      } else {
+        Ws[0][c][r] = (n < N && k < ke) ? weight_row(w, n, K)[k] : 0.f;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < BK; ++c) {
+      float a[4], b[DUAL ? 2 : 1][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[c][ty * 4 + i];
+#pragma unroll
+      for (int d = 0; d < (DUAL ? 2 : 1); ++d)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[d][j] = Ws[d][c][tx * 4 + j];
+#pragma unroll
+      for (int d = 0; d < (DUAL ? 2 : 1); ++d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[d][i][j] = fmaf(a[i], b[d][j], acc[d][i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int m = m0 + ty * 4 + i, n = n0 + tx * 4;
+    if (m >= M || n >= N) continue;
+    f32x4 v = {acc[0][i][0], acc[0][i][1], acc[0][i][2], acc[0][i][3]};
+    if (DUAL) {
+      f32x4 v3 = {acc[DUAL ? 1 : 0][i][0], acc[DUAL ? 1 : 0][i][1], acc[DUAL ? 1 : 0][i][2],
+                  acc[DUAL ? 1 : 0][i][3]};
+      if (SPLIT) {
+        float* p = partial + ((int64_t)blockIdx.z * M + m) * (2 * (int64_t)N);
+        *(f32x4*)(p + n) = v;
+        *(f32x4*)(p + N + n) = v3;
+      } else {
+        if constexpr (DUAL) epi(m, n, v, v3);
+      }
+    } else {
+      if (SPLIT)
+        *(f32x4*)(partial + ((int64_t)blockIdx.z * M + m) * (int64_t)N + n) = v;
+      else if constexpr (!DUAL)
+        epi(m, n, v);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ split-K reduce
+template <bool DUAL, class Epi>
+__global__ void __launch_bounds__(kThreads)
+splitk_reduce(const float* __restrict__ partial, int splits, int M, int N, Epi epi) {
+  const int64_t groups = (int64_t)M * (N / 4);
+  for (int64_t gi = (int64_t)blockIdx.x * kThreads + threadIdx.x; gi < groups;
+       gi += (int64_t)gridDim.x * kThreads) {
+    int m = (int)(gi / (N / 4));
+    int n = (int)(gi % (N / 4)) * 4;
+    const int64_t row = DUAL ? 2 * (int64_t)N : (int64_t)N;
+    const int64_t stride = (int64_t)M * row;
+    f32x4 s = {}, s3 = {};
+    const float* p = partial + (int64_t)m * row + n;
+    for (int z = 0; z < splits; ++z) {
+      s += *(const f32x4*)(p + z * stride);
+      if (DUAL) s3 += *(const f32x4*)(p + z * stride + N);
+    }
+    if constexpr (DUAL)
+      epi(m, n, s, s3);
+    else
+      epi(m, n, s);
+  }
+}
+
+// ------------------------------------------------------------------ launch
+template <int BM, int BN, int WM_, int WN_, bool DUAL, class Epi>
+hipError_t launch_mfma(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, int N, int K, Epi epi,
+                       int splits, float* partial, hipStream_t st) {
+  constexpr int BK = 64;
+  const int bn_out = DUAL ? BN / 2 : BN;
+  const int tiles = ((M + BM - 1) / BM) * ((N + bn_out - 1) / bn_out);
+  int kps = (K + splits - 1) / splits;
+  kps = (kps + BK - 1) / BK * BK;
+  dim3 grid(tiles, 1, splits);
+  if (splits > 1)
+    gemm_bf16_mfma<BM, BN, BK, WM_, WN_, DUAL, true, Epi>
+        <<<grid, kThreads, 0, st>>>(A, lda, w, M, N, K, kps, epi, partial);
+  else
+    gemm_bf16_mfma<BM, BN, BK, WM_, WN_, DUAL, false, Epi>
+        <<<grid, kThreads, 0, st>>>(A, lda, w, M, N, K, kps, epi, partial);
+  return hipGetLastError();
+}
+
+template <bool DUAL, class Epi>
+hipError_t launch_bf16(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, int N, int K, Epi epi,
+                       int splits, float* partial, hipStream_t st) {
+  hipError_t e;
+  if (M <= 32) {
+    if constexpr (DUAL)
+      e = launch_mfma<32, 256, 1, 4, DUAL>(A, lda, w, M, N, K, epi, splits, partial, st);
+    else
+      e = launch_mfma<32, 128, 1, 4, DUAL>(A, lda, w, M, N, K, epi, splits, partial, st);
+  } else if (M <= 64) {
+    e = launch_mfma<64, 256, 2, 2, DUAL>(A, lda, w, M, N, K, epi, splits, partial, st);
+  } else {
+    e = launch_mfma<256, 256, 2, 2, DUAL>(A, lda, w, M, N, K, epi, splits, partial, st);
+  }
+  if (e != hipSuccess || splits <= 1) return e;
+  int groups = (int)(((int64_t)M * (N / 4) + kThreads - 1) / kThreads);
+  splitk_reduce<DUAL, Epi><<<min(groups, 4096), kThreads, 0, st>>>(partial, splits, M, N, epi);
+  return hipGetLastError();
+}
+
+template <bool DUAL, class Epi>
+hipError_t launch_f32(const float* A, int64_t lda, WeightRows<float> w, int M, int N, int K, Epi epi,
+                      int splits, float* partial, hipStream_t st) {
+  const int tiles = ((M + 63) / 64) * ((N + 63) / 64);
+  int kps = (K + splits - 1) / splits;
+  kps = (kps + 15) / 16 * 16;
+  dim3 grid(tiles, 1, splits);
+  if (splits > 1)
+    gemm_f32_fma<DUAL, true, Epi><<<grid, kThreads, 0, st>>>(A, lda, w, M, N, K, kps, epi, partial);
+  else
+    gemm_f32_fma<DUAL, false, Epi><<<grid, kThreads, 0, st>>>(A, lda, w, M, N, K, kps, epi, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits <= 1) return e;
+  int groups = (int)(((int64_t)M * (N / 4) + kThreads - 1) / kThreads);
+  splitk_reduce<DUAL, Epi><<<min(groups, 4096), kThreads, 0, st>>>(partial, splits, M, N, epi);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int gemm_pick_splits(int M, int N, int K, bool dual, bool is_bf16) {
+  if (M > 64) return 1;
+  // small token count: the weights stream from HBM; split K until there are
+  // enough workgroups in flight to cover all 256 CUs several times over
+  int bn = is_bf16 ? (dual ? 128 : (M <= 32 ? 128 : 256)) : 64;
+  if (is_bf16 && M > 32) bn = dual ? 128 : 256;
+  int tiles = (N + bn - 1) / bn;
+  int bk = is_bf16 ? 64 : 16;
+  int max_splits = K / (bk * 4);  // keep >= 4 k-tiles per split
+  int s = 1;
+  while (tiles * s < 1024 && s * 2 <= max_splits && s < 32) s *= 2;
+  return s;
+}
+
+template <typename T, class Epi>
+hipError_t gemm_launch(const T* A, int64_t lda, WeightRows<T> w, int M, int N, int K, Epi epi,
+                       int splits, float* partial, hipStream_t st) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if constexpr (sizeof(T) == 2)
+    return launch_bf16<false>(A, lda, w, M, N, K, epi, splits, partial, st);
+  else
+    return launch_f32<false>(A, lda, w, M, N, K, epi, splits, partial, st);
+}
+
+template <typename T, class Epi>
+hipError_t gemm_dual_launch(const T* A, int64_t lda, const T* w1, const T* w3, int M, int N, int K,
+                            Epi epi, int splits, float* partial, hipStream_t st) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  WeightRows<T> w{w1, w3, nullptr, N, N};
+  if constexpr (sizeof(T) == 2)
+    return launch_bf16<true>(A, lda, w, M, N, K, epi, splits, partial, st);
+  else
+    return launch_f32<true>(A, lda, w, M, N, K, epi, splits, partial, st);
+}
+
+#define LLAMA_GEMM_INST(T)                                                                      \
+  template hipError_t gemm_launch<T, EpiStore<T>>(const T*, int64_t, WeightRows<T>, int, int, int, \
+                                                  EpiStore<T>, int, float*, hipStream_t);       \
+  template hipError_t gemm_launch<T, EpiResidual<T>>(const T*, int64_t, WeightRows<T>, int, int,   \
+                                                     int, EpiResidual<T>, int, float*,          \
+                                                     hipStream_t);                              \
+  template hipError_t gemm_launch<T, EpiQKV<T>>(const T*, int64_t, WeightRows<T>, int, int, int,   \
+                                                EpiQKV<T>, int, float*, hipStream_t);           \
+  template hipError_t gemm_launch<T, EpiF32>(const T*, int64_t, WeightRows<T>, int, int, int,      \
+                                             EpiF32, int, float*, hipStream_t);                 \
+  template hipError_t gemm_dual_launch<T, EpiSwiGLU<T>>(const T*, int64_t, const T*, const T*, int, \
+                                                        int, int, EpiSwiGLU<T>, int, float*,     \
+                                                        hipStream_t);
+
+LLAMA_GEMM_INST(bf16)
+LLAMA_GEMM_INST(float)
+
+}  // namespace llama

@@ -1,0 +1,111 @@
+// Projection GEMMs of the decoder block: C[m][n] = sum_k A[m][k] * W[n][k]
+// (nn.Linear, y = x W^T) with fused epilogues.  Declarations shared by the
+// launch layer; the kernels live in gemm.hip.
+#pragma once
+
+#include "common.hpp"
+
+namespace llama {
+
+// Where weight row n of the virtual [N][K] operand lives.  Plain GEMMs use w0
+// only (n1 = n2 = N).  The QKV projection concatenates wq | wk | wv: rows
+// [0, n1) from w0, [n1, n2) from w1, [n2, N) from w2.
+template <typename T>
+struct WeightRows {
+  const T* w0;
+  const T* w1;
+  const T* w2;
+  int n1, n2;
+};
+
+// Epilogues receive 4 consecutive output columns n..n+3 of row m in fp32.
+template <typename T>
+struct EpiStore {
+  T* y;
+  int64_t ldy;
+  __device__ __forceinline__ void operator()(int m, int n, f32x4 v) const {
+    store4(y + (int64_t)m * ldy + n, v);
+  }
+};
+
+// y = r + acc (the residual add of TransformerBlock.forward); y may equal r.
+template <typename T>
+struct EpiResidual {
+  T* y;
+  const T* r;
+  int64_t ld;
+  __device__ __forceinline__ void operator()(int m, int n, f32x4 v) const {
+    int64_t o = (int64_t)m * ld + n;
+    f32x4 rv = load4(r + o);
+    store4(y + o, rv + v);
+  }
+};
+
+// fp32 output (LM-head logits).
+struct EpiF32 {
+  float* y;
+  int64_t ldy;
+  __device__ __forceinline__ void operator()(int m, int n, f32x4 v) const {
+    store4(y + (int64_t)m * ldy + n, v);
+  }
+};
+
+// QKV epilogue: columns [0, nq) are q, [nq, nq+nkv) are k, the rest v.  q and k
+// get the interleaved-pair rotation of their position (start_pos + m % seqlen)
+// from the fp32 (cos, sin) table; q goes to q_out [M][nq]; k and v are written
+// straight into the caches at [b][start_pos + s] (cache append).
+template <typename T>
+struct EpiQKV {
+  T* q_out;
+  T* cache_k;
+  T* cache_v;
+  const float* freqs;  // [freqs_end][head_dim/2][2]
+  int seqlen, start_pos, max_seq, nq, nkv, head_dim;
+  __device__ __forceinline__ f32x4 rope(f32x4 v, int pos, int e) const {
+    const float* f = freqs + ((int64_t)pos * (head_dim >> 1) + (e >> 1)) * 2;
+    f32x4 cs = *(const f32x4*)f;  // cos_i, sin_i, cos_{i+1}, sin_{i+1}
+    return f32x4{v[0] * cs[0] - v[1] * cs[1], v[0] * cs[1] + v[1] * cs[0],
+                 v[2] * cs[2] - v[3] * cs[3], v[2] * cs[3] + v[3] * cs[2]};
+  }
+  __device__ __forceinline__ void operator()(int m, int n, f32x4 v) const {
+    int b = m / seqlen, s = m - b * seqlen;
+    int pos = start_pos + s;
+    if (n < nq) {
+      store4(q_out + (int64_t)m * nq + n, rope(v, pos, n % head_dim));
+    } else if (n < nq + nkv) {
+      int c = n - nq;
+      store4(cache_k + ((int64_t)b * max_seq + pos) * nkv + c, rope(v, pos, c % head_dim));
+    } else {
+      int c = n - nq - nkv;
+      store4(cache_v + ((int64_t)b * max_seq + pos) * nkv + c, v);
+    }
+  }
+};
+
+// SwiGLU epilogue: g = silu(a1) * a3 with a1 = (x w1^T), a3 = (x w3^T).
+template <typename T>
+struct EpiSwiGLU {
+  T* g;
+  int64_t ldg;
+  __device__ __forceinline__ void operator()(int m, int n, f32x4 a1, f32x4 a3) const {
+    f32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = a1[i] / (1.0f + __expf(-a1[i])) * a3[i];
+    store4(g + (int64_t)m * ldg + n, o);
+  }
+};
+
+// Host-side launch helpers (gemm.hip).  `splits` > 1 runs split-K: partial
+// sums go to `partial` (fp32, splits * M * N_out * (dual ? 2 : 1) floats) and a
+// second kernel reduces them and applies the epilogue.
+template <typename T, class Epi>
+hipError_t gemm_launch(const T* A, int64_t lda, WeightRows<T> w, int M, int N, int K, Epi epi,
+                       int splits, float* partial, hipStream_t st);
+template <typename T, class Epi>
+hipError_t gemm_dual_launch(const T* A, int64_t lda, const T* w1, const T* w3, int M, int N,
+                            int K, Epi epi, int splits, float* partial, hipStream_t st);
+
+// Split count the launch layer uses for an M x N x K problem (1 for large M).
+int gemm_pick_splits(int M, int N, int K, bool dual, bool bf16);
+
+}  // namespace llama

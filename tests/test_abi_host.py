@@ -1,0 +1,141 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and its
+host-only helpers and argument validation behave as documented.  No call here
+reaches a kernel launch (every device call below fails validation first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decoder_block_amd as dba
+from decoder_block_amd import _lib as L
+from oracle import block as ob
+import workloads as wl
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "llama_block.h")
+
+
+def declared_functions():
+    src = open(HEADER, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(llama_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = dba.lib()
+    names = declared_functions()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(L.EXPORTS) == names
+
+
+def args_for(w: wl.Workload, **kw):
+    a = dba.ModelArgs(dim=w.dim, n_heads=w.n_heads, n_kv_heads=w.n_kv_heads, multiple_of=w.multiple_of,
+                      ffn_dim_multiplier=w.ffn_dim_multiplier, norm_eps=w.norm_eps, rope_theta=w.rope_theta,
+                      max_batch_size=w.batch, max_seq_len=max(w.max_seq_len, 1))
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_ffn_hidden_dim_matches_oracle_and_workloads():
+    for w in wl.WORKLOADS.values():
+        assert dba.llama_ffn_hidden_dim(args_for(w)) == w.ffn_hidden
+        assert ob.ffn_hidden_dim(w.dim, w.multiple_of, w.ffn_dim_multiplier) == w.ffn_hidden
+    for dim in (64, 256, 1000, 5120, 6656, 8192):
+        for mo in (1, 32, 256):
+            for mult in (None, 1.3, 2.0):
+                a = dba.ModelArgs(dim=dim, n_heads=1, multiple_of=mo, ffn_dim_multiplier=mult)
+                # float multiplier at the ABI: compare with the oracle fed the same float32 value
+                m32 = None if mult is None else float(ctypes.c_float(mult).value)
+                assert dba.llama_ffn_hidden_dim(a) == ob.ffn_hidden_dim(dim, mo, m32)
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, 7):
+        assert isinstance(dba.status_str(s), str) and dba.status_str(s)
+
+
+def test_workspace_sizes_cover_the_intermediates():
+    w = wl.WORKLOADS[3]
+    a = args_for(w)
+    n = w.prefill_len
+    need = dba.llama_block_workspace_size(a, 1, n, 0, dba.LLAMA_BF16)
+    D, F = w.dim, w.ffn_hidden
+    assert need >= 2 * n * (4 * D + F)  # xn, q, o, h, hn (H*d = D) and the gated activation
+    dec = dba.llama_block_workspace_size(a, 1, 1, n, dba.LLAMA_BF16)
+    assert dec >= dba.llama_attn_decode_workspace_size(a, 1, n)
+    with pytest.raises(dba.LlamaError):
+        dba.llama_block_workspace_size(a, 2, 1, 0, dba.LLAMA_BF16)   # bsz > max_batch_size
+    with pytest.raises(dba.LlamaError):
+        dba.llama_block_workspace_size(a, 1, w.max_seq_len + 1, 0, dba.LLAMA_BF16)
+
+
+def _raw_block_forward(a, **over):
+    """Call llama_block_forward through ctypes with dummy non-null pointers."""
+    lib = dba.lib()
+    fake = 1 << 20                       # 16-byte aligned, never dereferenced: validation fails first
+    kw = dict(bsz=1, seqlen=4, start_pos=0, freqs_end=16, ws_bytes=0, dtype=dba.LLAMA_BF16, weights=None,
+              x=fake, out=fake * 2, ck=fake, cv=fake, freqs=fake, ws=fake)
+    kw.update(over)
+    w = kw["weights"] or L.CBlockWeights(*([fake] * 9))
+    return lib.llama_block_forward(ctypes.byref(a.c()), ctypes.byref(w), kw["ck"], kw["cv"], kw["freqs"],
+                                   kw["freqs_end"], kw["x"], kw["out"], kw["bsz"], kw["seqlen"], kw["start_pos"],
+                                   kw["ws"], kw["ws_bytes"], kw["dtype"], None)
+
+
+def test_block_forward_validation_errors():
+    a = dba.ModelArgs(dim=256, n_heads=2, n_kv_heads=1, max_batch_size=2, max_seq_len=16)
+    E, U, W = dba._lib.LLAMA_ERR_INVALID_ARG, dba._lib.LLAMA_ERR_UNSUPPORTED, dba._lib.LLAMA_ERR_WORKSPACE_TOO_SMALL
+    assert _raw_block_forward(a) == W                       # valid call, workspace missing
+    assert _raw_block_forward(a, bsz=3) == E                 # bsz > max_batch_size
+    assert _raw_block_forward(a, bsz=0) == E
+    assert _raw_block_forward(a, seqlen=0) == E
+    assert _raw_block_forward(a, start_pos=-1) == E
+    assert _raw_block_forward(a, start_pos=13) == E          # start_pos + seqlen > max_seq_len
+    assert _raw_block_forward(a, freqs_end=3) == E           # RoPE table too short
+    assert _raw_block_forward(a, x=None) == E
+    assert _raw_block_forward(a, ck=None) == E
+    assert _raw_block_forward(a, out=(1 << 20) + 64) == E    # out overlaps x
+    assert _raw_block_forward(a, x=(1 << 20) + 2) == E       # misaligned
+    assert _raw_block_forward(a, dtype=7) == E
+    bad = L.CBlockWeights(*([1 << 20] * 8 + [None]))
+    assert _raw_block_forward(a, weights=bad) == E
+    assert _raw_block_forward(dba.ModelArgs(dim=256, n_heads=3, max_batch_size=2, max_seq_len=16)) == E  # dim % H
+    assert _raw_block_forward(dba.ModelArgs(dim=256, n_heads=4, n_kv_heads=3, max_batch_size=2,
+                                            max_seq_len=16)) == E                    # H % Hkv
+    assert _raw_block_forward(dba.ModelArgs(dim=256, n_heads=8, max_batch_size=2, max_seq_len=16)) == U  # d=32 bf16
+    assert _raw_block_forward(dba.ModelArgs(dim=256, n_heads=8, max_batch_size=2, max_seq_len=16),
+                              dtype=dba.LLAMA_F32) == W                             # d=32 is built for f32
+
+
+def test_device_entry_points_reject_bad_arguments():
+    lib = dba.lib()
+    E = dba._lib.LLAMA_ERR_INVALID_ARG
+    p = 1 << 20
+    assert lib.llama_rmsnorm(None, p, p, 4, 256, 1e-5, dba.LLAMA_BF16, None) == E
+    assert lib.llama_rmsnorm(p, p, p, 4, 250, 1e-5, dba.LLAMA_BF16, None) == E       # dim % 8
+    assert lib.llama_rmsnorm(p, p, p, -1, 256, 1e-5, dba.LLAMA_BF16, None) == E
+    assert lib.llama_rmsnorm(None, None, None, 0, 256, 1e-5, dba.LLAMA_BF16, None) == 0  # empty: no-op
+    assert lib.llama_rope(p, p, p, 8, 1, 9, 0, 4, 4, 64, dba.LLAMA_BF16, None) == E     # table too short
+    assert lib.llama_rope(p, p, p, 64, 1, 9, 0, 4, 4, 66, dba.LLAMA_BF16, None) == E    # head_dim % 4
+    assert lib.llama_rope_freqs(None, 64, 10, 1e4, None) == E
+    assert lib.llama_rope_freqs(p, 63, 10, 1e4, None) == E
+    assert lib.llama_linear(p, p, p, 4, 100, 64, dba.LLAMA_BF16, None) == E            # in % 8
+    assert lib.llama_linear(p, p, p, 4, 128, 66, dba.LLAMA_BF16, None) == E            # out % 4
+    assert lib.llama_linear(None, None, None, 0, 128, 64, dba.LLAMA_BF16, None) == 0   # empty
+    a = dba.ModelArgs(dim=512, n_heads=4, n_kv_heads=2, max_batch_size=2, max_seq_len=8)
+    c = ctypes.byref(a.c())
+    assert lib.llama_gqa_attn_prefill(p, p, p, p, p, p, c, 1, 9, 0, dba.LLAMA_BF16, None) == E
+    assert lib.llama_gqa_attn_prefill(p, None, p, p, p, p, c, 1, 4, 0, dba.LLAMA_BF16, None) == E
+    assert lib.llama_gqa_attn_decode(p, p, p, p, p, p, c, 1, 8, p, 1 << 30, dba.LLAMA_BF16, None) == E
+    assert lib.llama_gqa_attn_decode(p, p, p, p, p, p, c, 3, 5, p, 1 << 30, dba.LLAMA_BF16, None) == E
+    big = dba.ModelArgs(dim=8192, n_heads=64, n_kv_heads=8, max_batch_size=1, max_seq_len=9000)
+    assert dba.llama_attn_decode_workspace_size(big, 1, 8000) > 0
+    assert lib.llama_gqa_attn_decode(p, p, p, p, p, p, ctypes.byref(big.c()), 1, 8000, p, 16, dba.LLAMA_BF16,
+                                     None) == dba._lib.LLAMA_ERR_WORKSPACE_TOO_SMALL
+    assert lib.llama_swiglu_ffn(p, p, p, p, p, 4, 256, 768, p, 0, dba.LLAMA_BF16, None) == \
+        dba._lib.LLAMA_ERR_WORKSPACE_TOO_SMALL
+    assert lib.llama_embedding(p, p, p, 4, 250, 10, dba.LLAMA_BF16, None) == E
+    assert lib.llama_lm_head_argmax(p, 100, p, p, p, p, 2, 256, 1000, 1e-5, p, 1 << 30, dba.LLAMA_BF16, None) == E

@@ -1,0 +1,226 @@
+"""Parity of each C entry point against the CPU oracle on seeded inputs (GPU).
+
+Shapes span several tiles and ragged tails; every call goes through the C ABI
+(via the ctypes binding) and every expected value comes from ``oracle``.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import decoder_block_amd as dba
+import workloads as wl
+from oracle import block as ob
+from tests.gpu_util import check, f64, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+_tid = [100]
+
+
+def rnd(shape, std=1.0, dtype="bf16"):
+    _tid[0] += 1
+    return wl.normal(tuple(shape), std, dtype, 0, 0, _tid[0])
+
+
+def dev(t):
+    return t.to("cuda:0")
+
+
+def tdt(dtype):
+    return wl.torch_dtype(dtype)
+
+
+# ----------------------------------------------------------------------------- RMSNorm
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,dim", [(37, 256), (129, 4096), (5, 8192), (3, 20480)])
+def test_rmsnorm(dtype, rows, dim):
+    need_gpu()
+    print(f"case rmsnorm {dtype} rows={rows} dim={dim}", flush=True)
+    x = rnd((rows, dim), 1.0, dtype) * 3
+    w = (1.0 + rnd((dim,), 0.2, dtype)).to(tdt(dtype))
+    x = x.to(tdt(dtype))
+    y = torch.empty_like(x, device="cuda:0")
+    dba.llama_rmsnorm(dev(x), dev(w), y, rows, dim, 1e-5)
+    torch.cuda.synchronize()
+    ref = ob.rms_norm(f64(x), f64(w), 1e-5)
+    check(y, ref, dtype, f"rmsnorm {dtype} {rows}x{dim}")
+
+
+# ----------------------------------------------------------------------------- RoPE
+@pytest.mark.parametrize("head_dim,end,theta", [(128, 16640, 5e5), (64, 4096, 1e4), (32, 200, 1e4)])
+def test_rope_table(head_dim, end, theta):
+    need_gpu()
+    print(f"case rope_freqs d={head_dim} end={end} theta={theta}", flush=True)
+    f = torch.empty(end, head_dim // 2, 2, device="cuda:0")
+    dba.llama_rope_freqs(f, head_dim, end, theta)
+    torch.cuda.synchronize()
+    ang = ob.rope_angles(head_dim, range(end), theta)
+    got = f64(f)
+    # fp64 evaluation rounded once to fp32: within half an fp32 ulp of 1
+    assert np.max(np.abs(got[..., 0] - np.cos(ang))) < 1e-7
+    assert np.max(np.abs(got[..., 1] - np.sin(ang))) < 1e-7
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rope_apply(dtype):
+    need_gpu()
+    B, S, H, Hkv, d, p0 = 2, 37, 8, 2, 128, 11
+    print(f"case rope {dtype}", flush=True)
+    end = 2 * (p0 + S)
+    f = torch.empty(end, d // 2, 2, device="cuda:0")
+    dba.llama_rope_freqs(f, d, end, 5e5)
+    xq = rnd((B, S, H, d), 1.0, dtype)
+    xk = rnd((B, S, Hkv, d), 1.0, dtype)
+    gq, gk = dev(xq), dev(xk)
+    dba.llama_rope(gq, gk, f, end, B, S, p0, H, Hkv, d)
+    torch.cuda.synchronize()
+    pos = list(range(p0, p0 + S))
+    check(gq, ob.apply_rope(f64(xq), pos, 5e5), dtype, "rope q")
+    check(gk, ob.apply_rope(f64(xk), pos, 5e5), dtype, "rope k")
+
+
+# ----------------------------------------------------------------------------- GEMM
+@pytest.mark.parametrize("dtype,M,K,N", [
+    ("bf16", 5, 256, 100),        # skinny path, ragged N
+    ("bf16", 50, 520, 388),       # 64-row path, K tail (520 = 8*64 + 8)
+    ("bf16", 300, 1024, 1000),    # large tiles with ragged M and N
+    ("bf16", 1024, 4096, 1536),   # several full 256x256 tiles
+    ("f32", 70, 260, 132),
+])
+def test_linear(dtype, M, K, N):
+    need_gpu()
+    print(f"case linear {dtype} M={M} K={K} N={N}", flush=True)
+    x = rnd((M, K), 1.0, dtype)
+    w = rnd((N, K), 0.05, dtype)
+    y = torch.empty(M, N, dtype=tdt(dtype), device="cuda:0")
+    dba.llama_linear(dev(x), dev(w), y, M, K, N)
+    torch.cuda.synchronize()
+    check(y, ob.linear(f64(x), f64(w)), dtype, f"linear {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("dtype,rows,dim,hidden", [
+    ("bf16", 300, 256, 768), ("bf16", 20, 512, 1536), ("bf16", 64, 256, 776), ("f32", 40, 256, 768)])
+def test_swiglu_ffn(dtype, rows, dim, hidden):
+    need_gpu()
+    print(f"case swiglu {dtype} rows={rows} dim={dim} hidden={hidden}", flush=True)
+    x = rnd((rows, dim), 1.0, dtype)
+    w1, w3 = rnd((hidden, dim), 0.05, dtype), rnd((hidden, dim), 0.05, dtype)
+    w2 = rnd((dim, hidden), 0.05, dtype)
+    y = torch.empty(rows, dim, dtype=tdt(dtype), device="cuda:0")
+    nbytes = dba.llama_ffn_workspace_size(rows, dim, hidden, dba.LLAMA_BF16 if dtype == "bf16" else dba.LLAMA_F32)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda:0")
+    dba.llama_swiglu_ffn(dev(x), dev(w1), dev(w3), dev(w2), y, rows, dim, hidden, ws, nbytes)
+    torch.cuda.synchronize()
+    check(y, ob.swiglu_ffn(f64(x), f64(w1), f64(w3), f64(w2)), dtype, "swiglu")
+
+
+# ----------------------------------------------------------------------------- attention
+def _args(H, Hkv, d, maxB, maxS, dtype_dim_mult=1):
+    return dba.ModelArgs(dim=H * d, n_heads=H, n_kv_heads=Hkv, multiple_of=256, max_batch_size=maxB,
+                         max_seq_len=maxS)
+
+
+@pytest.mark.parametrize("dtype,B,S,p0,H,Hkv,d", [
+    ("bf16", 2, 77, 0, 8, 8, 128),      # MHA, ragged query block
+    ("bf16", 1, 300, 0, 8, 2, 128),     # GQA n_rep 4
+    ("bf16", 2, 130, 50, 16, 2, 128),   # GQA n_rep 8, chunked prefill (start_pos > 0)
+    ("bf16", 1, 200, 0, 4, 1, 64),      # MQA, head_dim 64
+    ("bf16", 1, 64, 0, 32, 2, 64),      # n_rep 16 (two head groups per kv head)
+    ("f32", 1, 40, 9, 8, 2, 32),
+])
+def test_attn_prefill(dtype, B, S, p0, H, Hkv, d):
+    need_gpu()
+    print(f"case attn_prefill {dtype} B={B} S={S} p0={p0} H={H} Hkv={Hkv} d={d}", flush=True)
+    maxS = p0 + S + 3
+    args = _args(H, Hkv, d, B + 1, maxS)
+    q = rnd((B, S, H, d), 1.0, dtype)
+    k = rnd((B, S, Hkv, d), 1.0, dtype)
+    v = rnd((B, S, Hkv, d), 1.0, dtype)
+    ck = torch.zeros(B + 1, maxS, Hkv, d, dtype=tdt(dtype))
+    cv = torch.zeros_like(ck)
+    if p0:
+        ck[:, :p0] = rnd((B + 1, p0, Hkv, d), 1.0, dtype)
+        cv[:, :p0] = rnd((B + 1, p0, Hkv, d), 1.0, dtype)
+    gck, gcv = dev(ck), dev(cv)
+    out = torch.empty(B, S, H * d, dtype=tdt(dtype), device="cuda:0")
+    dba.llama_gqa_attn_prefill(dev(q), dev(k), dev(v), gck, gcv, out, args, B, S, p0)
+    torch.cuda.synchronize()
+    rck, rcv = f64(ck), f64(cv)
+    rck[:B, p0:p0 + S] = f64(k)
+    rcv[:B, p0:p0 + S] = f64(v)
+    np.testing.assert_array_equal(f64(gck), rck)   # append is a copy: bit-exact
+    np.testing.assert_array_equal(f64(gcv), rcv)
+    ref = ob.gqa_attention(f64(q), rck, rcv, p0)
+    check(out, ref, dtype, "attn prefill")
+
+
+@pytest.mark.parametrize("dtype,B,p0,H,Hkv,d", [
+    ("bf16", 3, 0, 8, 2, 128),       # single key
+    ("bf16", 2, 40, 8, 8, 128),      # MHA, short
+    ("bf16", 4, 4096, 64, 8, 128),   # 70B-shaped group, long context
+    ("bf16", 1, 8300, 32, 8, 128),   # many splits
+    ("bf16", 2, 999, 4, 1, 64),      # MQA head_dim 64
+    ("bf16", 1, 500, 32, 1, 128),    # n_rep 32 (two head groups)
+    ("f32", 2, 79, 8, 2, 32),
+])
+def test_attn_decode(dtype, B, p0, H, Hkv, d):
+    need_gpu()
+    print(f"case attn_decode {dtype} B={B} p0={p0} H={H} Hkv={Hkv} d={d}", flush=True)
+    maxS = p0 + 2
+    args = _args(H, Hkv, d, B, maxS)
+    q = rnd((B, 1, H, d), 1.0, dtype)
+    k = rnd((B, 1, Hkv, d), 1.0, dtype)
+    v = rnd((B, 1, Hkv, d), 1.0, dtype)
+    ck = torch.zeros(B, maxS, Hkv, d, dtype=tdt(dtype))
+    cv = torch.zeros_like(ck)
+    if p0:
+        ck[:, :p0] = rnd((B, p0, Hkv, d), 1.0, dtype)
+        cv[:, :p0] = rnd((B, p0, Hkv, d), 1.0, dtype)
+    gck, gcv = dev(ck), dev(cv)
+    out = torch.empty(B, 1, H * d, dtype=tdt(dtype), device="cuda:0")
+    nbytes = dba.llama_attn_decode_workspace_size(args, B, p0)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda:0")
+    dba.llama_gqa_attn_decode(dev(q), dev(k), dev(v), gck, gcv, out, args, B, p0, ws, nbytes)
+    torch.cuda.synchronize()
+    rck, rcv = f64(ck), f64(cv)
+    rck[:, p0] = f64(k)[:, 0]
+    rcv[:, p0] = f64(v)[:, 0]
+    np.testing.assert_array_equal(f64(gck), rck)
+    ref = ob.gqa_attention(f64(q), rck, rcv, p0)
+    check(out, ref, dtype, "attn decode")
+
+
+# ----------------------------------------------------------------------------- config-5 pieces
+def test_embedding_and_lm_head_argmax():
+    need_gpu()
+    print("case embedding + lm_head", flush=True)
+    V, D, B = 1000, 256, 6
+    table = rnd((V, D), 0.02)
+    tok = torch.tensor([0, 999, 5, 17, 5, 300], dtype=torch.int32)
+    out = torch.empty(B, D, dtype=torch.bfloat16, device="cuda:0")
+    dba.llama_embedding(dev(tok), dev(table), out, B, D, V)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(f64(out), f64(table)[tok.numpy()])
+    h = rnd((B, 3, D), 1.0)             # take the last of 3 rows per sequence (row stride 3*D)
+    w_out = rnd((V, D), 0.05)
+    w_out[77] = w_out[500]              # an exact tie: ids 77 and 500 give equal logits
+    norm_w = torch.ones(D, dtype=torch.bfloat16)
+    logits = torch.empty(B, V, dtype=torch.float32, device="cuda:0")
+    nxt = torch.empty(B, dtype=torch.int32, device="cuda:0")
+    nbytes = dba.llama_lm_head_workspace_size(B, D, V, dba.LLAMA_BF16)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda:0")
+    gh = dev(h)
+    dba.llama_lm_head_argmax(gh[:, 2], 3 * D, dev(norm_w), dev(w_out), logits, nxt, B, D, V, 1e-5, ws, nbytes)
+    torch.cuda.synchronize()
+    ref = ob.linear(ob.rms_norm(f64(h)[:, 2], f64(norm_w), 1e-5), f64(w_out))
+    e = check(logits, ref, "bf16", "lm head logits")
+    got = nxt.cpu().numpy()
+    lg = f64(logits)
+    assert np.all(lg[:, 77] == lg[:, 500])
+    for b in range(B):
+        # the argmax of the GPU's own logits, lowest id on ties (exact, integer)
+        assert got[b] == int(np.argmax(lg[b]))
+        # and a correct greedy token against the exact logits (margin rule)
+        assert ref[b, got[b]] >= ref[b].max() - 2 * e["raw_maxabs"]
