@@ -1,0 +1,287 @@
+"""Benchmark of the LLaMA decoder-block forward pass on one MI355X.
+
+One step = one ``llama_block_forward`` prefill call of the LLaMA-7B-shaped
+block (dim 4096, 32 heads, FFN 11008, bf16) over batch 4 x 2048 tokens: every
+step of the hot path (RMSNorm, QKV + RoPE + cache append, causal attention,
+wo + residual, RMSNorm, w1/w3 + SwiGLU, w2 + residual) on seeded synthetic
+inputs already resident in HBM.  ``value`` is prefill tokens/s for the block.
+
+Also reported on the same line: per-stage times from HIP events recorded on
+the launch stream, the MFMA roofline fraction of the dominant kernel, the
+Llama-3-8B-shaped prefill (1 x 8192) and decode steps (1 x T = 8193..) and the
+Llama-2-70B-shaped batch-32 decode step with its attention kernel's HBM
+roofline fraction, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "prefill tokens/s per block + decode step µs; % of MFMA / HBM roofline"
+STAGES = ["attention_norm", "qkv_rope_append", "attention", "wo_residual", "ffn_norm", "w1w3_swiglu",
+          "w2_residual"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def stage_work(w, bsz, S, p0):
+    """Algorithmic flops (GEMMs, attention) and bytes (norms) per stage for one call."""
+    D, H, Hkv, d, F = w.dim, w.n_heads, w.n_kv_heads, w.head_dim, w.ffn_hidden
+    N = bsz * S
+    causal_keys = sum(p0 + s + 1 for s in range(S)) if S > 1 else (p0 + 1)
+    return {
+        "attention_norm": ("hbm", 2 * N * D * 2 + 2 * D),
+        "qkv_rope_append": ("mfma", 2 * N * D * (H + 2 * Hkv) * d),
+        "attention": ("mfma", 4 * bsz * H * d * causal_keys),
+        "wo_residual": ("mfma", 2 * N * H * d * D),
+        "ffn_norm": ("hbm", 2 * N * D * 2 + 2 * D),
+        "w1w3_swiglu": ("mfma", 4 * N * D * F),
+        "w2_residual": ("mfma", 2 * N * F * D),
+    }
+
+
+def decode_bytes(w, bsz, T):
+    """HBM bytes of one decode step: weights once, KV cache read, activations."""
+    D, H, Hkv, d, F = w.dim, w.n_heads, w.n_kv_heads, w.head_dim, w.ffn_hidden
+    weights = 2 * (D * (H + 2 * Hkv) * d + H * d * D + 3 * D * F) + 4 * D
+    kv = 2 * 2 * bsz * T * Hkv * d
+    return weights, kv
+
+
+def make_runner(wid, dev, cache=None):
+    import torch
+    import workloads as wl
+    from decoder_block_amd.runner import BlockRunner, model_args_for
+    w = wl.WORKLOADS[wid]
+    wts = wl.block_weights(w)
+    r = BlockRunner(model_args_for(w), wts, torch.bfloat16, dev, cache=cache)
+    return w, wts, r
+
+
+def time_prefill(r, x, steps, warmup, p0=0):
+    import torch
+    bsz, S, _ = x.shape
+    r.reserve(bsz, S, p0)
+    out = torch.empty_like(x)
+    for _ in range(warmup):
+        r.forward(x, p0, out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        r.forward(x, p0, out)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    # per-stage durations from HIP events recorded on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(steps)]
+    for e in evs:
+        r.forward(x, p0, out, events=e)
+    torch.cuda.synchronize()
+    stage_ms = [sum(e[i - 1].elapsed_time(e[i]) for e in evs) / steps for i in range(1, 8)]
+    return wall, stage_ms
+
+
+def flush_mall(buf):
+    buf.add_(1)  # 512 MiB write evicts the 256 MB Infinity Cache between decode reps
+
+
+def time_decode(r, xs, p0s, flush):
+    """Times each one-token call separately with events (MALL flushed before each)."""
+    import torch
+    bsz = xs[0].shape[0]
+    r.reserve(bsz, 1, max(p0s))
+    out = torch.empty_like(xs[0])
+    tot, stage_tot = [], [0.0] * 7
+    for x, p0 in zip(xs, p0s):
+        flush_mall(flush)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+        r.forward(x, p0, out, events=e)
+        torch.cuda.synchronize()
+        tot.append(e[0].elapsed_time(e[7]))
+        for i in range(1, 8):
+            stage_tot[i - 1] += e[i - 1].elapsed_time(e[i])
+    n = len(xs)
+    return tot, [s / n for s in stage_tot]
+
+
+def kernel_traffic(kernel_key):
+    """HBM traffic per launch from the committed rocprofv3 PMC summary, or None when the
+    kernel source changed since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        with open(p) as f:
+            d = json.load(f)
+        ent = d[kernel_key]
+        src = os.path.join(ROOT, ent["source"])
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        return ent["bytes_per_launch"] if h == ent["source_sha256_16"] else None
+    except Exception:
+        return None
+
+
+def cpu_baseline(w, wts, x):
+    """The oracle (numpy float64) on the same workload (a few seconds of BLAS work on the host)."""
+    import numpy as np
+    import torch
+    from oracle import block as ob
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:
+        cores = os.cpu_count() or 1
+    S, B = w.prefill_len, w.batch
+    W = {k: v.to(torch.float64).numpy() for k, v in wts.items()}
+    xs = x[:, :S].to(torch.float64).numpy()
+    ck = np.zeros((B, S, w.n_kv_heads, w.head_dim))
+    cv = np.zeros_like(ck)
+    t0 = time.perf_counter()
+    ob.block_forward(xs, W, ck, cv, 0, w.n_heads, w.n_kv_heads, w.norm_eps, w.rope_theta)
+    dt = time.perf_counter() - t0
+    return {"value": B * S / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"the whole {w.name} workload ({B} x {S}-token prefill), numpy float64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=16, help="timed one-token calls per decode workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true", help="skip the extra workloads (profiling runs)")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported (this build has no multi-GPU "
+              f"path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as wl
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+
+    # ---------------------------------------------------------------- headline: 7B-shaped block prefill
+    log("workload llama7b-block-prefill: generating inputs")
+    w2, wts2, r2 = make_runner(2, dev)
+    x2 = wl.activations(w2).to(dev)
+    tokens = w2.batch * w2.prefill_len
+    log(f"timing {a.steps} steps after {a.warmup} warmup")
+    wall, stage_ms = time_prefill(r2, x2, a.steps, a.warmup)
+    work = stage_work(w2, w2.batch, w2.prefill_len, 0)
+    stages = {}
+    for name, ms in zip(STAGES, stage_ms):
+        kind, amount = work[name]
+        if kind == "mfma":
+            ach = amount / (ms * 1e-3) / 1e12
+            stages[name] = {"ms": round(ms, 4), "tflops": round(ach, 1), "mfma_frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+        else:
+            ach = amount / (ms * 1e-3) / 1e9
+            stages[name] = {"ms": round(ms, 4), "gbs": round(ach, 1), "hbm_frac": round(ach / PEAK_HBM_GBS, 4)}
+    dom = "w1w3_swiglu"
+    dom_ms = stage_ms[STAGES.index(dom)]
+    dom_ach = work[dom][1] / (dom_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "gemm_bf16_mfma<DUAL> (w1/w3 + SwiGLU epilogue)",
+                "achieved": round(dom_ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dom_ach / PEAK_BF16_TFLOPS, 4), "traffic": kernel_traffic("w1w3_swiglu_llama7b"),
+                "kernel_ms": round(dom_ms, 4)}
+    total_gemm_attn = sum(work[n][1] for n in STAGES if work[n][0] == "mfma")
+    block_ach = total_gemm_attn / wall / 1e12
+    extra = {"block_tflops": round(block_ach, 1), "block_mfma_frac": round(block_ach / PEAK_BF16_TFLOPS, 4),
+             "stages": stages}
+    del r2
+    torch.cuda.empty_cache()
+
+    if not a.prefill_only:
+        flush = torch.zeros(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+        # ------------------------------------------------------------ 8B-shaped prefill 8192 + decode
+        log("workload llama3-8b-block: prefill 8192 then decode steps")
+        w3, wts3, r3 = make_runner(3, dev)
+        x3 = wl.activations(w3).to(dev)
+        S3 = w3.prefill_len
+        xp = x3[:, :S3].contiguous()
+        wall3, stage3 = time_prefill(r3, xp, max(3, a.steps // 4), 1)
+        work3 = stage_work(w3, 1, S3, 0)
+        att = work3["attention"][1] / (stage3[2] * 1e-3) / 1e12
+        pre3 = {"tokens_per_s": round(S3 / wall3, 1), "ms": round(wall3 * 1e3, 3),
+                "attention_ms": round(stage3[2], 4), "attention_tflops": round(att, 1),
+                "attention_mfma_frac": round(att / PEAK_BF16_TFLOPS, 4),
+                "gemm_mfma_frac": round(sum(work3[n][1] for n in ("qkv_rope_append", "wo_residual", "w1w3_swiglu",
+                                                                   "w2_residual")) /
+                                        (sum(stage3[i] for i in (1, 3, 5, 6)) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        nd = min(a.decode_steps, w3.decode_steps)
+        xs = [x3[:, S3 + t:S3 + t + 1].contiguous() for t in range(nd)]
+        tot, st = time_decode(r3, xs, [S3 + t for t in range(nd)], flush)
+        wb, kvb = decode_bytes(w3, 1, S3 + nd // 2)
+        attn_gbs = kvb / (st[2] * 1e-3) / 1e9
+        dec3 = {"step_us_mean": round(1e3 * sum(tot) / len(tot), 2),
+                "step_us_median": round(1e3 * sorted(tot)[len(tot) // 2], 2),
+                "attention_us": round(st[2] * 1e3, 2), "attention_gbs": round(attn_gbs, 1),
+                "attention_hbm_frac": round(attn_gbs / PEAK_HBM_GBS, 4),
+                "step_gbs": round((wb + kvb) / (sum(tot) / len(tot) * 1e-3) / 1e9, 1),
+                "steps_timed": nd, "positions": [S3, S3 + nd - 1]}
+        del r3
+        torch.cuda.empty_cache()
+        # ------------------------------------------------------------ 70B-shaped batch-32 decode
+        log("workload llama2-70b-block-decode: batch 32 at position 4096")
+        w4 = wl.WORKLOADS[4]
+        cache = wl.prefilled_cache(w4)
+        w4, wts4, r4 = make_runner(4, dev, cache=cache)
+        x4 = wl.activations(w4).to(dev)
+        p0 = w4.cache_prefill
+        tot4 = []
+        st4 = [0.0] * 7
+        for _ in range(max(a.decode_steps, 3)):
+            # the same token at the same position each rep: the append rewrites identical rows
+            t, s = time_decode(r4, [x4], [p0], flush)
+            tot4 += t
+            st4 = [u + v for u, v in zip(st4, s)]
+        n4 = len(tot4)
+        st4 = [u / n4 for u in st4]
+        wb4, kvb4 = decode_bytes(w4, w4.batch, p0 + 1)
+        attn4 = kvb4 / (st4[2] * 1e-3) / 1e9
+        dec4 = {"step_us_mean": round(1e3 * sum(tot4) / n4, 2),
+                "step_us_median": round(1e3 * sorted(tot4)[n4 // 2], 2),
+                "attention_us": round(st4[2] * 1e3, 2), "attention_gbs": round(attn4, 1),
+                "attention_hbm_frac": round(attn4 / PEAK_HBM_GBS, 4),
+                "step_gbs": round((wb4 + kvb4) / (sum(tot4) / n4 * 1e-3) / 1e9, 1),
+                "step_hbm_frac": round((wb4 + kvb4) / (sum(tot4) / n4 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "stage_us": {n: round(v * 1e3, 2) for n, v in zip(STAGES, st4)}}
+        del r4, flush
+        torch.cuda.empty_cache()
+        extra.update({"llama3_8b_prefill_8192": pre3, "llama3_8b_decode": dec3, "llama2_70b_decode_b32": dec4})
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("cpu baseline: oracle on the same workload")
+        cpu = cpu_baseline(w2, wts2, wl.activations(w2))
+
+    line = {
+        "metric": METRIC, "value": round(tokens / wall, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
+        "config": {"workload": w2.name, "dim": w2.dim, "n_heads": w2.n_heads, "n_kv_heads": w2.n_kv_heads,
+                   "ffn_hidden": w2.ffn_hidden, "batch": w2.batch, "seq_len": w2.prefill_len,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        **extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -28,7 +28,7 @@ EXPORTS = (
     "llama_status_str", "llama_ffn_hidden_dim", "llama_block_workspace_size",
     "llama_attn_decode_workspace_size", "llama_ffn_workspace_size", "llama_rope_freqs",
     "llama_rmsnorm", "llama_rope", "llama_gqa_attn_prefill", "llama_gqa_attn_decode",
-    "llama_swiglu_ffn", "llama_linear", "llama_block_forward", "llama_embedding",
+    "llama_swiglu_ffn", "llama_linear", "llama_block_forward", "llama_block_forward_events", "llama_embedding",
     "llama_lm_head_workspace_size", "llama_lm_head_argmax",
 )
 
@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
             "llama_linear": ([P, P, P, I64, I32, I32, ctypes.c_int, P], ctypes.c_int),
             "llama_block_forward": ([A, ctypes.POINTER(CBlockWeights), P, P, P, I32, P, P, I32, I32, I32, P, SZ,
                                      ctypes.c_int, P], ctypes.c_int),
+            "llama_block_forward_events": ([A, ctypes.POINTER(CBlockWeights), P, P, P, I32, P, P, I32, I32, I32, P,
+                                            SZ, ctypes.c_int, P, ctypes.POINTER(P)], ctypes.c_int),
             "llama_embedding": ([P, P, P, I64, I32, I32, ctypes.c_int, P], ctypes.c_int),
             "llama_lm_head_argmax": ([P, I64, P, P, P, P, I32, I32, I32, F, P, SZ, ctypes.c_int, P], ctypes.c_int),
         }
@@ -230,6 +232,25 @@ def llama_block_forward(args: ModelArgs, weights, cache_k, cache_v, freqs, freqs
     _check(lib().llama_block_forward(ctypes.byref(args.c()), ctypes.byref(w), _ptr(cache_k), _ptr(cache_v),
                                      _ptr(freqs), freqs_end, _ptr(x), _ptr(out), bsz, seqlen, start_pos, _ptr(ws),
                                      ws_bytes, _dtype(x), _stream(stream)), "llama_block_forward")
+
+
+def llama_block_forward_events(args: ModelArgs, weights, cache_k, cache_v, freqs, freqs_end: int, x, out, bsz: int,
+                               seqlen: int, start_pos: int, ws, ws_bytes: int, events, stream=None) -> None:
+    """``events``: 8 torch.cuda.Event(enable_timing=True) (or raw hipEvent_t handles)."""
+    w = weights if isinstance(weights, CBlockWeights) else block_weights(weights)
+    st = _stream(stream)
+    handles = []
+    for e in events:
+        if isinstance(e, int):
+            handles.append(e)
+        else:
+            if not e.cuda_event:
+                e.record()  # torch creates the HIP event on first use
+            handles.append(e.cuda_event)
+    arr = (ctypes.c_void_p * 8)(*handles)
+    _check(lib().llama_block_forward_events(ctypes.byref(args.c()), ctypes.byref(w), _ptr(cache_k), _ptr(cache_v),
+                                            _ptr(freqs), freqs_end, _ptr(x), _ptr(out), bsz, seqlen, start_pos,
+                                            _ptr(ws), ws_bytes, _dtype(x), st, arr), "llama_block_forward_events")
 
 
 def llama_embedding(tokens, table, out, n: int, dim: int, vocab: int, stream=None) -> None:

@@ -113,7 +113,10 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 template <typename T>
 int block_forward_t(const Dims& g, const llama_model_args* a, const llama_block_weights* w, T* ck, T* cv,
                     const float* freqs, const T* x, T* out, int bsz, int seqlen, int start_pos, char* ws,
-                    const BlockWs& L, hipStream_t st) {
+                    const BlockWs& L, hipStream_t st, hipEvent_t* ev) {
+  // ev (optional): ev[0] before the first stage, ev[i] after stage i (i = 1..7)
+  auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
+  if (mark(0) != hipSuccess) return LLAMA_ERR_HIP;
   const int M = bsz * seqlen;
   T* xn = (T*)(ws + L.xn);
   T* q = (T*)(ws + L.q);
@@ -128,41 +131,41 @@ int block_forward_t(const Dims& g, const llama_model_args* a, const llama_block_
   hipError_t e;
   // h = x + wo(attention(RMSNorm(x)))
   e = llama::rmsnorm<T>(x, g.D, (const T*)w->attention_norm, xn, M, g.D, a->norm_eps, st);
-  if (e != hipSuccess) return LLAMA_ERR_HIP;
+  if (e != hipSuccess || mark(1) != hipSuccess) return LLAMA_ERR_HIP;
   {
     llama::WeightRows<T> wr{(const T*)w->wq, (const T*)w->wk, (const T*)w->wv, nq, nq + nkv};
     llama::EpiQKV<T> epi{q, ck, cv, freqs, seqlen, start_pos, a->max_seq_len, nq, nkv, g.d};
     const int N = nq + 2 * nkv;
     e = llama::gemm_launch<T>(xn, g.D, wr, M, N, g.D, epi, llama::gemm_pick_splits(M, N, g.D, false, bf), part, st);
-    if (e != hipSuccess) return LLAMA_ERR_HIP;
+    if (e != hipSuccess || mark(2) != hipSuccess) return LLAMA_ERR_HIP;
   }
   llama::AttnShape sh{bsz, seqlen, start_pos, g.H, g.Hkv, g.d, a->max_seq_len};
   if (seqlen == 1)
     e = llama::attn_decode<T>(q, ck, cv, o, sh, part, st);
   else
     e = llama::attn_prefill<T>(q, ck, cv, o, sh, st);
-  if (e != hipSuccess) return LLAMA_ERR_HIP;
+  if (e != hipSuccess || mark(3) != hipSuccess) return LLAMA_ERR_HIP;
   {
     llama::WeightRows<T> wr{(const T*)w->wo, nullptr, nullptr, g.D, g.D};
     llama::EpiResidual<T> epi{h, x, g.D};
     e = llama::gemm_launch<T>(o, nq, wr, M, g.D, nq, epi, llama::gemm_pick_splits(M, g.D, nq, false, bf), part, st);
-    if (e != hipSuccess) return LLAMA_ERR_HIP;
+    if (e != hipSuccess || mark(4) != hipSuccess) return LLAMA_ERR_HIP;
   }
   // out = h + w2(silu(w1 hn) * w3 hn), hn = RMSNorm(h)
   e = llama::rmsnorm<T>(h, g.D, (const T*)w->ffn_norm, hn, M, g.D, a->norm_eps, st);
-  if (e != hipSuccess) return LLAMA_ERR_HIP;
+  if (e != hipSuccess || mark(5) != hipSuccess) return LLAMA_ERR_HIP;
   {
     llama::EpiSwiGLU<T> epi{gt, g.F};
     e = llama::gemm_dual_launch<T>(hn, g.D, (const T*)w->w1, (const T*)w->w3, M, g.F, g.D, epi,
                                    llama::gemm_pick_splits(M, g.F, g.D, true, bf), part, st);
-    if (e != hipSuccess) return LLAMA_ERR_HIP;
+    if (e != hipSuccess || mark(6) != hipSuccess) return LLAMA_ERR_HIP;
   }
   {
     llama::WeightRows<T> wr{(const T*)w->w2, nullptr, nullptr, g.D, g.D};
     llama::EpiResidual<T> epi{out, h, g.D};
     e = llama::gemm_launch<T>(gt, g.F, wr, M, g.D, g.F, epi, llama::gemm_pick_splits(M, g.D, g.F, false, bf), part,
                               st);
-    if (e != hipSuccess) return LLAMA_ERR_HIP;
+    if (e != hipSuccess || mark(7) != hipSuccess) return LLAMA_ERR_HIP;
   }
   (void)dt;
   return LLAMA_OK;
@@ -389,9 +392,10 @@ int llama_swiglu_ffn(const void* x, const void* w1, const void* w3, const void* 
   return hip_status(e);
 }
 
-int llama_block_forward(const llama_model_args* a, const llama_block_weights* w, void* cache_k, void* cache_v,
-                        const float* freqs, int32_t freqs_end, const void* x, void* out, int32_t bsz, int32_t seqlen,
-                        int32_t start_pos, void* ws, size_t ws_bytes, llama_dtype dt, llama_stream_t stream) {
+static int block_forward_impl(const llama_model_args* a, const llama_block_weights* w, void* cache_k, void* cache_v,
+                              const float* freqs, int32_t freqs_end, const void* x, void* out, int32_t bsz,
+                              int32_t seqlen, int32_t start_pos, void* ws, size_t ws_bytes, llama_dtype dt,
+                              llama_stream_t stream, hipEvent_t* ev) {
   Dims g;
   int rc = model_dims(a, dt, &g);
   if (rc != LLAMA_OK) return rc;
@@ -411,9 +415,27 @@ int llama_block_forward(const llama_model_args* a, const llama_block_weights* w,
   hipStream_t st = (hipStream_t)stream;
   if (dt == LLAMA_BF16)
     return block_forward_t<bf16>(g, a, w, (bf16*)cache_k, (bf16*)cache_v, freqs, (const bf16*)x, (bf16*)out, bsz,
-                                 seqlen, start_pos, (char*)ws, L, st);
+                                 seqlen, start_pos, (char*)ws, L, st, ev);
   return block_forward_t<float>(g, a, w, (float*)cache_k, (float*)cache_v, freqs, (const float*)x, (float*)out, bsz,
-                                seqlen, start_pos, (char*)ws, L, st);
+                                seqlen, start_pos, (char*)ws, L, st, ev);
+}
+
+int llama_block_forward(const llama_model_args* a, const llama_block_weights* w, void* cache_k, void* cache_v,
+                        const float* freqs, int32_t freqs_end, const void* x, void* out, int32_t bsz, int32_t seqlen,
+                        int32_t start_pos, void* ws, size_t ws_bytes, llama_dtype dt, llama_stream_t stream) {
+  return block_forward_impl(a, w, cache_k, cache_v, freqs, freqs_end, x, out, bsz, seqlen, start_pos, ws, ws_bytes,
+                            dt, stream, nullptr);
+}
+
+int llama_block_forward_events(const llama_model_args* a, const llama_block_weights* w, void* cache_k,
+                               void* cache_v, const float* freqs, int32_t freqs_end, const void* x, void* out,
+                               int32_t bsz, int32_t seqlen, int32_t start_pos, void* ws, size_t ws_bytes,
+                               llama_dtype dt, llama_stream_t stream, void* const* events) {
+  if (!events) return LLAMA_ERR_INVALID_ARG;
+  for (int i = 0; i < 8; ++i)
+    if (!events[i]) return LLAMA_ERR_INVALID_ARG;
+  return block_forward_impl(a, w, cache_k, cache_v, freqs, freqs_end, x, out, bsz, seqlen, start_pos, ws, ws_bytes,
+                            dt, stream, (hipEvent_t*)events);
 }
 
 int llama_embedding(const int32_t* tokens, const void* table, void* out, int64_t n, int32_t dim, int32_t vocab,

@@ -200,6 +200,18 @@ int llama_block_forward(const llama_model_args* args, const llama_block_weights*
                         const void* x, void* out, int32_t bsz, int32_t seqlen, int32_t start_pos,
                         void* ws, size_t ws_bytes, llama_dtype dtype, llama_stream_t stream);
 
+/* llama_block_forward with stage timing: identical arguments and results, plus
+ * `events`, 8 caller-created hipEvent_t handles recorded on `stream`: events[0]
+ * before the first kernel and events[i] after stage i, the stages being
+ * 1 attention_norm, 2 QKV projection + RoPE + cache append, 3 attention,
+ * 4 wo + residual, 5 ffn_norm, 6 w1/w3 + SwiGLU, 7 w2 + residual.
+ * hipEventElapsedTime(events[i-1], events[i]) is stage i's duration. */
+int llama_block_forward_events(const llama_model_args* args, const llama_block_weights* weights,
+                               void* cache_k, void* cache_v, const float* freqs_cis,
+                               int32_t freqs_end, const void* x, void* out, int32_t bsz,
+                               int32_t seqlen, int32_t start_pos, void* ws, size_t ws_bytes,
+                               llama_dtype dtype, llama_stream_t stream, void* const* events);
+
 /* Token embedding lookup (notes, section 3, Transformer.forward, tok_embeddings):
  * out[i] = table[tokens[i]].  tokens: device int32 [n]; table: device [vocab][dim];
  * out: device [n][dim].  Ids outside [0, vocab) produce a zero row (checked on the

@@ -1,0 +1,170 @@
+"""Whole-block parity at the workloads' real shapes and GPU-side invariants (GPU).
+
+The block runs through ``llama_block_forward``; the oracle evaluates the same
+seeded inputs.  At full size the oracle evaluates sampled output rows (each
+output row has its own definition) and the whole KV cache.  A decode step at
+position p equals the prefill row at p (pinned on the oracle by
+test_kv_cache_decode_equals_full_prefill), so decode rows are checked against
+the oracle's rows of one call over all positions.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from decoder_block_amd.runner import BlockRunner, model_args_for
+from oracle import block as ob
+from tests.gpu_util import check, f64, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _w64(wts):
+    return {k: v.to(torch.float64).numpy() for k, v in wts.items()}
+
+
+def _rows(S, extra=()):
+    r = {0, 1, 2, 63, 64, 127, 128, 255, 256, S // 2, S - 2, S - 1, *extra}
+    return sorted(x for x in r if 0 <= x < S)
+
+
+def test_tiny_f32_prefill_then_decode_steps():
+    dev = need_gpu()
+    w = wl.WORKLOADS[1]
+    print(f"case {w.name}: prefill {w.prefill_len} + {w.decode_steps} decode steps (f32)", flush=True)
+    wts = wl.block_weights(w)
+    x = wl.activations(w)
+    run = BlockRunner(model_args_for(w), wts, torch.float32, dev)
+    S = w.prefill_len
+    outs = [run.forward(x[:, :S].contiguous().to(dev), 0)]
+    for t in range(w.decode_steps):
+        outs.append(run.forward(x[:, S + t:S + t + 1].contiguous().to(dev), S + t))
+    torch.cuda.synchronize()
+    got = torch.cat(outs, dim=1)
+    W = _w64(wts)
+    shape = (w.batch, w.max_seq_len, w.n_kv_heads, w.head_dim)
+    ck, cv = np.zeros(shape), np.zeros(shape)
+    xr = f64(x)
+    ref = [ob.block_forward(xr[:, :S], W, ck, cv, 0, w.n_heads, w.n_kv_heads, w.norm_eps, w.rope_theta)]
+    for t in range(w.decode_steps):
+        ref.append(ob.block_forward(xr[:, S + t:S + t + 1], W, ck, cv, S + t, w.n_heads, w.n_kv_heads, w.norm_eps,
+                                    w.rope_theta))
+    check(got, np.concatenate(ref, axis=1), "f32", "tiny block outputs")
+    check(run.cache_k, ck, "f32", "tiny cache_k")
+    check(run.cache_v, cv, "f32", "tiny cache_v")
+
+
+def test_llama7b_block_prefill_full_size():
+    dev = need_gpu()
+    w = wl.WORKLOADS[2]
+    print(f"case {w.name}: B={w.batch} S={w.prefill_len} bf16", flush=True)
+    wts = wl.block_weights(w)
+    x = wl.activations(w)
+    run = BlockRunner(model_args_for(w), wts, torch.bfloat16, dev)
+    out = run.forward(x.to(dev), 0)
+    torch.cuda.synchronize()
+    rows = _rows(w.prefill_len)
+    shape = (w.batch, w.max_seq_len, w.n_kv_heads, w.head_dim)
+    ck, cv = np.zeros(shape), np.zeros(shape)
+    ref = ob.block_forward(f64(x), _w64(wts), ck, cv, 0, w.n_heads, w.n_kv_heads, w.norm_eps, w.rope_theta,
+                           rows=rows)
+    check(out[:, rows], ref, "bf16", "7B block sampled rows")
+    check(run.cache_k, ck, "bf16", "7B cache_k (k after RoPE)")
+    check(run.cache_v, cv, "bf16", "7B cache_v")
+
+
+def test_llama3_8b_block_prefill_then_128_decodes():
+    dev = need_gpu()
+    w = wl.WORKLOADS[3]
+    print(f"case {w.name}: prefill {w.prefill_len} + {w.decode_steps} decodes bf16", flush=True)
+    wts = wl.block_weights(w)
+    x = wl.activations(w)
+    run = BlockRunner(model_args_for(w), wts, torch.bfloat16, dev)
+    S = w.prefill_len
+    gx = x.to(dev)
+    pre = run.forward(gx[:, :S].contiguous(), 0)
+    dec = [run.forward(gx[:, S + t:S + t + 1].contiguous(), S + t) for t in range(w.decode_steps)]
+    torch.cuda.synchronize()
+    got = torch.cat([pre] + dec, dim=1)
+    rows = _rows(S, (4095, 4096)) + [S + t for t in (0, 1, 2, 31, 63, 64, 126, 127)]
+    shape = (w.batch, w.max_seq_len, w.n_kv_heads, w.head_dim)
+    ck, cv = np.zeros(shape), np.zeros(shape)
+    ref = ob.block_forward(f64(x), _w64(wts), ck, cv, 0, w.n_heads, w.n_kv_heads, w.norm_eps, w.rope_theta,
+                           rows=rows)
+    check(got[:, rows], ref, "bf16", "8B block sampled prefill + decode rows")
+    check(run.cache_k, ck, "bf16", "8B cache_k")
+    check(run.cache_v, cv, "bf16", "8B cache_v")
+
+
+def test_llama2_70b_block_decode_batch32():
+    dev = need_gpu()
+    w = wl.WORKLOADS[4]
+    print(f"case {w.name}: B={w.batch} decode at {w.cache_prefill} bf16", flush=True)
+    wts = wl.block_weights(w)
+    x = wl.activations(w)
+    ck0, cv0 = wl.prefilled_cache(w)
+    run = BlockRunner(model_args_for(w), wts, torch.bfloat16, dev, cache=(ck0, cv0))
+    out = run.forward(x.to(dev), w.cache_prefill)
+    torch.cuda.synchronize()
+    ck, cv = f64(ck0), f64(cv0)
+    ref = ob.block_forward(f64(x), _w64(wts), ck, cv, w.cache_prefill, w.n_heads, w.n_kv_heads, w.norm_eps,
+                           w.rope_theta)
+    check(out, ref, "bf16", "70B decode outputs")
+    p = w.cache_prefill
+    check(run.cache_k[:, p], ck[:, p], "bf16", "70B appended k")
+    check(run.cache_v[:, p], cv[:, p], "bf16", "70B appended v")
+    # rows before the append are untouched (bit-exact)
+    np.testing.assert_array_equal(f64(run.cache_k[:, :p]), f64(ck0[:, :p]))
+
+
+# ----------------------------------------------------------------------------- invariants
+SMALL = wl.Workload(30, "small-gqa", "bf16", 512, 8, 2, 1536, 256, None, 1e-5, 1e4, batch=3, prefill_len=100,
+                    decode_steps=6)
+
+
+def _small_runner(dev, batch=None):
+    w = SMALL
+    return BlockRunner(model_args_for(w, max_batch=batch or w.batch), wl.block_weights(w), torch.bfloat16, dev)
+
+
+def test_decode_chain_matches_prefill_and_oracle():
+    dev = need_gpu()
+    w = SMALL
+    x = wl.activations(w).to(dev)
+    a = w.prefill_len
+    full = _small_runner(dev).forward(x, 0)
+    r = _small_runner(dev)
+    parts = [r.forward(x[:, :a].contiguous(), 0)]
+    parts += [r.forward(x[:, a + t:a + t + 1].contiguous(), a + t) for t in range(w.decode_steps)]
+    chunk = _small_runner(dev)
+    c = [chunk.forward(x[:, :40].contiguous(), 0), chunk.forward(x[:, 40:].contiguous(), 40)]
+    torch.cuda.synchronize()
+    chain = torch.cat(parts, dim=1)
+    chunked = torch.cat(c, dim=1)
+    shape = (w.batch, w.max_seq_len, w.n_kv_heads, w.head_dim)
+    ck, cv = np.zeros(shape), np.zeros(shape)
+    ref = ob.block_forward(f64(x), _w64(wl.block_weights(w)), ck, cv, 0, w.n_heads, w.n_kv_heads, w.norm_eps,
+                           w.rope_theta)
+    check(full, ref, "bf16", "small prefill")
+    check(chain, ref, "bf16", "small prefill + decode chain")
+    check(chunked, ref, "bf16", "small chunked prefill")
+    check(chain, f64(full), "bf16", "chain vs full prefill (GPU vs GPU)")
+
+
+def test_determinism_batch_independence_causality():
+    dev = need_gpu()
+    w = SMALL
+    x = wl.activations(w)[:, :w.prefill_len].contiguous().to(dev)
+    r = _small_runner(dev)
+    o1 = r.forward(x, 0).clone()
+    o2 = r.forward(x, 0).clone()
+    assert torch.equal(o1, o2), "repeated runs differ"
+    one = _small_runner(dev, batch=1).forward(x[1:2].contiguous(), 0)
+    assert torch.equal(one, o1[1:2]), "batch rows are not independent"
+    t = 57
+    xp = x.clone()
+    xp[:, t] += 1.0
+    o3 = r.forward(xp, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(o3[:, :t], o1[:, :t]), "an output before the perturbed position changed"
+    assert not torch.equal(o3[:, t], o1[:, t])
