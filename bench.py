@@ -161,6 +161,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=16, help="timed one-token calls per decode workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="skip the extra workloads (profiling runs)")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="first run one plain 1 GiB device-to-device copy (scales rocprofv3 FETCH/WRITE_SIZE)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported (this build has no multi-GPU "
@@ -173,6 +175,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if a.calibration_copy:
+        src = torch.ones(1 << 29, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---------------------------------------------------------------- headline: 7B-shaped block prefill
     log("workload llama7b-block-prefill: generating inputs")

@@ -103,8 +103,11 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
   constexpr int KL = BKV * CHK / 256;         // K chunks per thread per tile
   constexpr int VT = 16 * CHK;                // V transpose tasks (4 keys x 8 d each)
   static_assert(HD == 64 || HD == 128, "head_dim");
-  __shared__ bf16x8 Ks[2][BKV * CHK];         // [key][chunk ^ (key & 7)]
-  __shared__ bf16x8 Vt[2][HD * (BKV / 8)];    // [d][key chunk ^ (d & 7)], keys permuted
+  // XOR swizzles: the 16 lanes of a ds_read_b128 phase (16 consecutive rows, one
+  // chunk) land on 16 distinct 16-byte bank groups of the 64-bank LDS
+  __shared__ bf16x8 Ks[2][BKV * CHK];         // [key][chunk ^ f(key)]
+  __shared__ bf16x8 Vt[2][HD * (BKV / 8)];    // [d][key chunk ^ ((d >> 1) & 7)], keys permuted
+  auto kswz = [](int key, int c) { return CHK == 16 ? (c ^ (key & 15)) : (c ^ ((key >> 1) & 7)); };
 
   const int H = sh.n_heads, Hkv = sh.n_kv_heads, S = sh.seqlen, p0 = sh.start_pos;
   const int n_rep = H / Hkv;
@@ -163,7 +166,7 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
     for (int i = 0; i < KL; ++i) {
       int key = tid / CHK + i * (256 / CHK);
       int c = tid % CHK;
-      Ks[buf][key * CHK + (c ^ (key & 7))] = kreg[i];
+      Ks[buf][key * CHK + kswz(key, c)] = kreg[i];
     }
     if (tid < VT) {
       int kg = tid / CHK, dc = tid % CHK;
@@ -175,7 +178,7 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
       for (int e8 = 0; e8 < 8; ++e8) {
         int d = dc * 8 + e8;
         bf16x4 v4 = {vreg[0][e8], vreg[1][e8], vreg[2][e8], vreg[3][e8]};
-        bf16* rowp = (bf16*)&Vt[buf][d * 8 + (pc ^ (d & 7))];
+        bf16* rowp = (bf16*)&Vt[buf][d * 8 + (pc ^ ((d >> 1) & 7))];
         *(bf16x4*)(rowp + off) = v4;
       }
     }
@@ -202,7 +205,7 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
 #pragma unroll
       for (int kk = 0; kk < HD / 16; ++kk) {
         const int c = kk * 2 + lhalf;
-        bf16x8 kf = Ks[buf][key * CHK + (c ^ (key & 7))];
+        bf16x8 kf = Ks[buf][key * CHK + kswz(key, c)];
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[kt], 0, 0, 0);
       }
     }
@@ -247,7 +250,7 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
 #pragma unroll
         for (int dt = 0; dt < HD / 32; ++dt) {
           const int d = dt * 32 + lrow;
-          bf16x8 vf = Vt[buf][d * 8 + (pc ^ (d & 7))];
+          bf16x8 vf = Vt[buf][d * 8 + (pc ^ ((d >> 1) & 7))];
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[dt], 0, 0, 0);
         }
       }
@@ -331,7 +334,7 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
       for (int dd = 0; dd < 8; ++dd) {
         const int d = vdc * 8 + dd;
         bf16x8 w = {vk[0][dd], vk[1][dd], vk[2][dd], vk[3][dd], vk[4][dd], vk[5][dd], vk[6][dd], vk[7][dd]};
-        Vt[wave][d * 4 + (vg ^ ((d >> 1) & 3))] = w;
+        Vt[wave][d * 4 + (vg ^ ((d >> 2) & 3))] = w;
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -375,7 +378,7 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
 #pragma unroll
     for (int dt = 0; dt < HD / 16; ++dt) {
       const int d = dt * 16 + l16;
-      bf16x8 vf = Vt[wave][d * 4 + (g ^ ((d >> 1) & 3))];
+      bf16x8 vf = Vt[wave][d * 4 + (g ^ ((d >> 2) & 3))];
       oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[dt] * alpha, 0, 0, 0);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -7,7 +7,8 @@
 // RoPE pairs and pair w1/w3 results in registers and store 8-byte vectors.
 // Both operands are K-contiguous (nn.Linear layout), which is the layout the
 // MFMA wants per lane (8 consecutive k values); tiles sit in LDS as 16-byte
-// chunks with an XOR swizzle on the chunk index to spread rows over banks.
+// chunks with an XOR swizzle on the chunk index so that the 16 lanes of one
+// ds_read_b128 phase (16 consecutive rows) cover all 64 banks.
 //
 // f32: a plain LDS-tiled FMA kernel (the fp32 workload is tiny and launch
 // bound), same epilogues.
@@ -18,6 +19,7 @@ namespace llama {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kStages = 4;   // LDS ring depth of the DMA-pipelined kernel
 
 template <typename T>
 __device__ __forceinline__ const T* weight_row(const WeightRows<T>& w, int n, int K) {
@@ -115,7 +117,7 @@ gemm_bf16_mfma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int 
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       int r = row_of[i];
-      smem[buf][r * CH + (chunk_of[i] ^ (r & 7))] = stage[i];
+      smem[buf][r * CH + (chunk_of[i] ^ ((r >> 1) & 7))] = stage[i];
     }
   };
 
@@ -150,12 +152,12 @@ gemm_bf16_mfma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int 
 #pragma unroll
       for (int t = 0; t < TN; ++t) {
         int r = BM + wrow(t) + lrow;
-        fa[t] = smem[buf][r * CH + (c ^ (r & 7))];
+        fa[t] = smem[buf][r * CH + (c ^ ((r >> 1) & 7))];
       }
 #pragma unroll
       for (int t = 0; t < TM; ++t) {
         int r = wm * WM + t * 32 + lrow;
-        fb[t] = smem[buf][r * CH + (c ^ (r & 7))];
+        fb[t] = smem[buf][r * CH + (c ^ ((r >> 1) & 7))];
       }
 #pragma unroll
       for (int a = 0; a < TN; ++a)
@@ -203,6 +205,185 @@ gemm_bf16_mfma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int 
           } else {
             epi(m, n, v);
           }
+        }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ bf16 MFMA kernel, LDS DMA pipeline
+// Large-M variant: 256 x 256 output tile, BK = 32, NS-stage ring of LDS tiles
+// filled by global_load_lds_dwordx4 (global memory straight into LDS, no
+// staging registers), so NS-1 k-tiles are in flight while one is consumed.
+// Each DMA instruction writes 1 KiB = 16 tile rows x 64 B; lane l of block b
+// fetches row b*16 + l/4, 16-byte chunk (l%4) ^ ((l/16)%4): the XOR swizzle
+// makes the 16 lanes of each ds_read_b128 phase (16 consecutive rows, one
+// chunk) hit 16 distinct 16-byte bank groups.  Rows past M or N read a
+// clamped (valid) row whose products land only in discarded outputs; K must
+// be a multiple of 32.
+// Schedule per k-tile: the fragments of each 16-deep half are read from LDS
+// while the previous half's 16 MFMAs run, the next tile's first half is read
+// right after the single s_barrier, and the DMA refill of the ring slot just
+// consumed is issued after that barrier.  The vmcnt waits are explicit: the
+// compiler cannot see the LDS writes of the DMA.
+#define LLAMA_LDS __attribute__((address_space(3)))
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  // s_waitcnt simm16 on gfx9: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(63 | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+template <int NS, bool DUAL, class Epi>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M, int N, int K, Epi epi) {
+  constexpr int BM = 256, BN = 256, BK = 32, CH = 4;
+  constexpr int WM = 128, WN = 128, TM = 4, TN = 4;
+  constexpr int ROWS = BM + BN;               // 512 rows x 64 B = 32 KiB per stage
+  constexpr int BLOCKS = ROWS / 16;           // 1 KiB DMA blocks per stage
+  constexpr int LOADS = BLOCKS / 4;           // per wave (and per lane) per stage
+  constexpr int BN_OUT = DUAL ? BN / 2 : BN;
+  static_assert(NS >= 3, "ring depth");
+  __shared__ bf16x8 smem[NS][ROWS * CH];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles_n = (N + BN_OUT - 1) / BN_OUT;
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN_OUT;
+  const int nk = K / BK;
+
+  // this lane's source row pointer (+ chunk offset) for each of its DMA blocks
+  const bf16* src[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int blk = wave * LOADS + i;
+    const int r = blk * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((lane >> 4) & 3);
+    const bf16* p;
+    if (r < BM) {
+      p = A + (int64_t)min(m0 + r, M - 1) * lda;
+    } else {
+      const int rb = r - BM;
+      if (DUAL) {
+        const int n = min(n0 + (rb & (BN / 2 - 1)), N - 1);
+        p = (rb < BN / 2 ? w.w0 : w.w1) + (int64_t)n * K;
+      } else {
+        p = weight_row(w, min(n0 + rb, N - 1), K);
+      }
+    }
+    src[i] = p + c * 8;
+  }
+  // DMA of k-tile kt into ring slot kt % NS (kt is clamped to the last tile so the
+  // refill at the end of the loop stays branch-free; those copies are never read)
+  auto issue = [&](int kt) {
+    const int st = kt % NS;
+    const int kc = min(kt, nk - 1);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      LLAMA_LDS void* dst = (LLAMA_LDS void*)&smem[st][(wave * LOADS + i) * 64];
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + kc * BK), dst, 16, 0, 0);
+    }
+  };
+  auto wrow = [&](int t) {
+    if (DUAL) return t < TN / 2 ? wn * (WN / 2) + t * 32 : BN / 2 + wn * (WN / 2) + (t - TN / 2) * 32;
+    return wn * WN + t * 32;
+  };
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  auto read_half = [&](int st, int kk, bf16x8* fa, bf16x8* fb) {
+    const int c = kk * 2 + lhalf;
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      const int r = BM + wrow(t) + lrow;
+      fa[t] = smem[st][r * CH + (c ^ ((r >> 2) & 3))];
+    }
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      const int r = wm * WM + t * 32 + lrow;
+      fb[t] = smem[st][r * CH + (c ^ ((r >> 2) & 3))];
+    }
+  };
+
+  f32x16 acc[TN][TM];
+#pragma unroll
+  for (int a = 0; a < TN; ++a)
+#pragma unroll
+    for (int b = 0; b < TM; ++b) acc[a][b] = f32x16{};
+  auto mfma_half = [&](const bf16x8* fa, const bf16x8* fb) {
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+#pragma unroll
+      for (int b = 0; b < TM; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+  };
+  // 8 fragment reads spread over 16 MFMAs
+  auto interleave = [&]() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+
+  bf16x8 fa0[TN], fb0[TM], fa1[TN], fb1[TM];
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue(s);
+  wait_vmcnt<(NS - 2) * LOADS>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  issue(NS - 1);
+  read_half(0, 0, fa0, fb0);
+
+  for (int kt = 0; kt < nk - 1; ++kt) {
+    const int st = kt % NS;
+    read_half(st, 1, fa1, fb1);
+    mfma_half(fa0, fb0);
+    interleave();
+    // tile kt+1 landed (NS-2 later tiles may still be in flight); our reads of slot st are done
+    wait_vmcnt<(NS - 2) * LOADS>();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(kt + NS);
+    read_half((kt + 1) % NS, 0, fa0, fb0);
+    mfma_half(fa1, fb1);
+    interleave();
+  }
+  read_half((nk - 1) % NS, 1, fa1, fb1);
+  mfma_half(fa0, fb0);
+  interleave();
+  mfma_half(fa1, fb1);
+  // no DMA may still be writing LDS when the workgroup retires
+  wait_vmcnt<0>();
+
+#pragma unroll
+  for (int b = 0; b < TM; ++b) {
+    const int m = m0 + wm * WM + b * 32 + lrow;
+    if (m >= M) continue;
+    if constexpr (DUAL) {
+#pragma unroll
+      for (int a = 0; a < TN / 2; ++a)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * (WN / 2) + a * 32 + g * 8 + lhalf * 4;
+          if (n >= N) continue;
+          f32x4 v1 = {acc[a][b][g * 4], acc[a][b][g * 4 + 1], acc[a][b][g * 4 + 2], acc[a][b][g * 4 + 3]};
+          const f32x16& a3 = acc[a + TN / 2][b];
+          f32x4 v3 = {a3[g * 4], a3[g * 4 + 1], a3[g * 4 + 2], a3[g * 4 + 3]};
+          epi(m, n, v1, v3);
+        }
+    } else {
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * WN + a * 32 + g * 8 + lhalf * 4;
+          if (n >= N) continue;
+          f32x4 v = {acc[a][b][g * 4], acc[a][b][g * 4 + 1], acc[a][b][g * 4 + 2], acc[a][b][g * 4 + 3]};
+          epi(m, n, v);
         }
     }
   }
@@ -338,6 +519,12 @@ hipError_t launch_bf16(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, in
   } else if (M <= 64) {
     e = launch_mfma<64, 256, 2, 2, DUAL>(A, lda, w, M, N, K, epi, splits, partial, st);
   } else {
+    if (splits <= 1 && K % 32 == 0 && lda % 8 == 0 && K / 32 >= 1) {
+      const int bn_out = DUAL ? 128 : 256;
+      const int tiles = ((M + 255) / 256) * ((N + bn_out - 1) / bn_out);
+      gemm_bf16_dma<kStages, DUAL, Epi><<<tiles, kThreads, 0, st>>>(A, lda, w, M, N, K, epi);
+      return hipGetLastError();
+    }
     e = launch_mfma<256, 256, 2, 2, DUAL>(A, lda, w, M, N, K, epi, splits, partial, st);
   }
   if (e != hipSuccess || splits <= 1) return e;

@@ -85,7 +85,9 @@ def test_rope_apply(dtype):
 @pytest.mark.parametrize("dtype,M,K,N", [
     ("bf16", 5, 256, 100),        # skinny path, ragged N
     ("bf16", 50, 520, 388),       # 64-row path, K tail (520 = 8*64 + 8)
-    ("bf16", 300, 1024, 1000),    # large tiles with ragged M and N
+    ("bf16", 300, 1024, 1000),    # large tiles with ragged M and N (LDS-DMA pipeline)
+    ("bf16", 200, 1000, 260),     # large tiles, K not a multiple of 32 (register-staged kernel)
+    ("bf16", 257, 64, 256),       # a single k-tile pair, one row past a tile
     ("bf16", 1024, 4096, 1536),   # several full 256x256 tiles
     ("f32", 70, 260, 132),
 ])
