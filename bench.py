@@ -153,6 +153,40 @@ def cpu_baseline(w, wts, x):
             "sample": f"the whole {w.name} workload ({B} x {S}-token prefill), numpy float64, {dt:.1f} s"}
 
 
+def bench_stack(dev, steps):
+    """32 layers + embedding + LM head: prefill of 64 x 2048 prompts, then greedy one-token steps."""
+    import torch
+    import workloads as wl
+    from decoder_block_amd.model import StackRunner
+    from decoder_block_amd.runner import model_args_for
+    w = wl.WORKLOADS[5]
+    log(f"workload {w.name}: generating {w.n_layers} layers")
+    emb, norm_w, w_out = wl.stack_tensors(w)
+    stack = StackRunner(model_args_for(w), lambda l: wl.block_weights(w, l), emb, norm_w, w_out, torch.bfloat16, dev)
+    prompt = wl.prompt_tokens(w).to(dev)
+    out = torch.empty(steps + 1, w.batch, dtype=torch.int32, device=dev)
+    logits = torch.empty(w.batch, w.vocab_size, dtype=torch.float32, device=dev)
+    stack.forward(prompt, 0, logits, out[0])          # warm-up (fills the caches)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record()
+    stack.forward(prompt, 0, logits, out[0])
+    e[1].record()
+    for t in range(steps):
+        stack.forward(out[t].view(w.batch, 1), w.prefill_len + t, logits, out[t + 1])
+    e[2].record()
+    torch.cuda.synchronize()
+    pre = e[0].elapsed_time(e[1])
+    dec = e[1].elapsed_time(e[2]) / steps
+    log(f"stack prefill {pre:.1f} ms, decode {dec:.3f} ms/step")
+    res = {"prefill_ms": round(pre, 2), "prefill_tokens_per_s": round(w.batch * w.prefill_len / pre * 1e3, 1),
+           "decode_ms_per_step": round(dec, 3), "decode_tokens_per_s": round(w.batch / dec * 1e3, 1),
+           "decode_steps_timed": steps, "batch": w.batch, "prompt": w.prefill_len, "layers": w.n_layers}
+    del stack
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,6 +195,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=16, help="timed one-token calls per decode workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="skip the extra workloads (profiling runs)")
+    ap.add_argument("--stack", action="store_true",
+                    help="also time the 32-layer Llama-3-8B-shaped stack: 64 x 2048 prefill + greedy steps")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (scales rocprofv3 FETCH/WRITE_SIZE)")
     a = ap.parse_args()
@@ -271,6 +307,9 @@ def main():
         del r4, flush
         torch.cuda.empty_cache()
         extra.update({"llama3_8b_prefill_8192": pre3, "llama3_8b_decode": dec3, "llama2_70b_decode_b32": dec4})
+
+    if a.stack:
+        extra["llama3_8b_stack"] = bench_stack(dev, a.decode_steps)
 
     cpu = None
     if not a.no_cpu_baseline:

@@ -73,7 +73,7 @@ size_t decode_partial_floats(const Dims& g, int bsz, int T, llama_dtype dt) {
 }
 
 struct BlockWs {
-  size_t xn, q, o, h, hn, g, partial, total;
+  size_t xn, q, o, h, hn, g, r1, r2, partial, total;
 };
 
 BlockWs block_ws_layout(const Dims& g, int bsz, int seqlen, int start_pos, llama_dtype dt) {
@@ -92,6 +92,8 @@ BlockWs block_ws_layout(const Dims& g, int bsz, int seqlen, int start_pos, llama
   w.h = take(N * g.D * es);
   w.hn = take(N * g.D * es);
   w.g = take(N * g.F * es);
+  w.r1 = take(N * sizeof(float));
+  w.r2 = take(N * sizeof(float));
   size_t pf = 0;
   const int M = (int)N;
   pf = std::max(pf, gemm_partial_floats(M, (g.H + 2 * g.Hkv) * g.d, g.D, false, dt));
@@ -124,17 +126,21 @@ int block_forward_t(const Dims& g, const llama_model_args* a, const llama_block_
   T* h = (T*)(ws + L.h);
   T* hn = (T*)(ws + L.hn);
   T* gt = (T*)(ws + L.g);
+  float* r1 = (float*)(ws + L.r1);
+  float* r2 = (float*)(ws + L.r2);
   float* part = (float*)(ws + L.partial);
   const bool bf = sizeof(T) == 2;
   const llama_dtype dt = bf ? LLAMA_BF16 : LLAMA_F32;
   const int nq = g.H * g.d, nkv = g.Hkv * g.d;
   hipError_t e;
-  // h = x + wo(attention(RMSNorm(x)))
-  e = llama::rmsnorm<T>(x, g.D, (const T*)w->attention_norm, xn, M, g.D, a->norm_eps, st);
+  // h = x + wo(attention(RMSNorm(x))).  RMSNorm(x) W^T is computed as
+  // rsqrt(mean(x^2) + eps) * ((x * g) W^T): the row factor is applied to the fp32
+  // accumulators, so the normalised activation is never rounded to bf16.
+  e = llama::rmsnorm<T>(x, g.D, (const T*)w->attention_norm, xn, M, g.D, a->norm_eps, st, r1);
   if (e != hipSuccess || mark(1) != hipSuccess) return LLAMA_ERR_HIP;
   {
     llama::WeightRows<T> wr{(const T*)w->wq, (const T*)w->wk, (const T*)w->wv, nq, nq + nkv};
-    llama::EpiQKV<T> epi{q, ck, cv, freqs, seqlen, start_pos, a->max_seq_len, nq, nkv, g.d};
+    llama::EpiQKV<T> epi{q, ck, cv, freqs, seqlen, start_pos, a->max_seq_len, nq, nkv, g.d, r1};
     const int N = nq + 2 * nkv;
     e = llama::gemm_launch<T>(xn, g.D, wr, M, N, g.D, epi, llama::gemm_pick_splits(M, N, g.D, false, bf), part, st);
     if (e != hipSuccess || mark(2) != hipSuccess) return LLAMA_ERR_HIP;
@@ -152,10 +158,10 @@ int block_forward_t(const Dims& g, const llama_model_args* a, const llama_block_
     if (e != hipSuccess || mark(4) != hipSuccess) return LLAMA_ERR_HIP;
   }
   // out = h + w2(silu(w1 hn) * w3 hn), hn = RMSNorm(h)
-  e = llama::rmsnorm<T>(h, g.D, (const T*)w->ffn_norm, hn, M, g.D, a->norm_eps, st);
+  e = llama::rmsnorm<T>(h, g.D, (const T*)w->ffn_norm, hn, M, g.D, a->norm_eps, st, r2);
   if (e != hipSuccess || mark(5) != hipSuccess) return LLAMA_ERR_HIP;
   {
-    llama::EpiSwiGLU<T> epi{gt, g.F};
+    llama::EpiSwiGLU<T> epi{gt, g.F, r2};
     e = llama::gemm_dual_launch<T>(hn, g.D, (const T*)w->w1, (const T*)w->w3, M, g.F, g.D, epi,
                                    llama::gemm_pick_splits(M, g.F, g.D, true, bf), part, st);
     if (e != hipSuccess || mark(6) != hipSuccess) return LLAMA_ERR_HIP;
@@ -374,7 +380,7 @@ int llama_swiglu_ffn(const void* x, const void* w1, const void* w3, const void* 
   if (bf) {
     bf16* g = (bf16*)wsb;
     e = llama::gemm_dual_launch<bf16>((const bf16*)x, dim, (const bf16*)w1, (const bf16*)w3, M, hidden, dim,
-                                      llama::EpiSwiGLU<bf16>{g, hidden}, s1, part, st);
+                                      llama::EpiSwiGLU<bf16>{g, hidden, nullptr}, s1, part, st);
     if (e == hipSuccess) {
       llama::WeightRows<bf16> wr{(const bf16*)w2, nullptr, nullptr, dim, dim};
       e = llama::gemm_launch<bf16>(g, hidden, wr, M, dim, hidden, llama::EpiStore<bf16>{(bf16*)y, dim}, s2, part, st);
@@ -382,7 +388,7 @@ int llama_swiglu_ffn(const void* x, const void* w1, const void* w3, const void* 
   } else {
     float* g = (float*)wsb;
     e = llama::gemm_dual_launch<float>((const float*)x, dim, (const float*)w1, (const float*)w3, M, hidden, dim,
-                                       llama::EpiSwiGLU<float>{g, hidden}, s1, part, st);
+                                       llama::EpiSwiGLU<float>{g, hidden, nullptr}, s1, part, st);
     if (e == hipSuccess) {
       llama::WeightRows<float> wr{(const float*)w2, nullptr, nullptr, dim, dim};
       e = llama::gemm_launch<float>(g, hidden, wr, M, dim, hidden, llama::EpiStore<float>{(float*)y, dim}, s2, part,

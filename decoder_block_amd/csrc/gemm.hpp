@@ -61,6 +61,7 @@ struct EpiQKV {
   T* cache_v;
   const float* freqs;  // [freqs_end][head_dim/2][2]
   int seqlen, start_pos, max_seq, nq, nkv, head_dim;
+  const float* rscale; // optional per-row RMSNorm factor applied to the accumulators
   __device__ __forceinline__ f32x4 rope(f32x4 v, int pos, int e) const {
     const float* f = freqs + ((int64_t)pos * (head_dim >> 1) + (e >> 1)) * 2;
     f32x4 cs = *(const f32x4*)f;  // cos_i, sin_i, cos_{i+1}, sin_{i+1}
@@ -68,6 +69,7 @@ struct EpiQKV {
                  v[2] * cs[2] - v[3] * cs[3], v[2] * cs[3] + v[3] * cs[2]};
   }
   __device__ __forceinline__ void operator()(int m, int n, f32x4 v) const {
+    if (rscale) v *= rscale[m];
     int b = m / seqlen, s = m - b * seqlen;
     int pos = start_pos + s;
     if (n < nq) {
@@ -87,7 +89,13 @@ template <typename T>
 struct EpiSwiGLU {
   T* g;
   int64_t ldg;
+  const float* rscale; // optional per-row RMSNorm factor applied to both accumulators
   __device__ __forceinline__ void operator()(int m, int n, f32x4 a1, f32x4 a3) const {
+    if (rscale) {
+      const float r = rscale[m];
+      a1 *= r;
+      a3 *= r;
+    }
     f32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = a1[i] / (1.0f + __expf(-a1[i])) * a3[i];

@@ -24,10 +24,13 @@ template <> struct Vec<float> {
 // RMSNorm (LLaMA notes, section 3, class RMSNorm): one workgroup per row; the
 // sum of squares is reduced in fp32 across the wavefront and then the four
 // waves; y = x * rsqrt(mean + eps) * w with a single rounding at the store.
+// With `rscale` set, the kernel stores y = x * w (one rounding; exact when w is
+// all ones) and the row factor rsqrt(mean + eps) in rscale[row], for a
+// projection that applies the factor to its fp32 accumulators.
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
 rmsnorm_kernel(const T* __restrict__ x, int64_t x_stride, const T* __restrict__ w, T* y, int dim,
-               float eps) {
+               float eps, float* __restrict__ rscale) {
   constexpr int V = Vec<T>::N;
   constexpr int CACHE = 4;
   typedef typename Vec<T>::type vec;
@@ -64,7 +67,9 @@ rmsnorm_kernel(const T* __restrict__ x, int64_t x_stride, const T* __restrict__ 
   float tot = 0.f;
 #pragma unroll
   for (int i = 0; i < kThreads / 64; ++i) tot += red[i];
-  const float r = 1.0f / sqrtf(tot / (float)dim + eps);
+  const float rr = 1.0f / sqrtf(tot / (float)dim + eps);
+  const float r = rscale ? 1.0f : rr;
+  if (rscale && threadIdx.x == 0) rscale[row] = rr;
   auto emit = [&](int i, const vec& v) {
     vec wv = *(const vec*)(w + i * V);
     vec o;
@@ -179,9 +184,9 @@ inline int grid_for(int64_t work, int per_block = kThreads) {
 
 template <typename T>
 hipError_t rmsnorm(const T* x, int64_t x_stride, const T* w, T* y, int64_t rows, int dim, float eps,
-                   hipStream_t st) {
+                   hipStream_t st, float* rscale) {
   if (rows == 0) return hipSuccess;
-  rmsnorm_kernel<T><<<(unsigned)rows, kThreads, 0, st>>>(x, x_stride, w, y, dim, eps);
+  rmsnorm_kernel<T><<<(unsigned)rows, kThreads, 0, st>>>(x, x_stride, w, y, dim, eps, rscale);
   return hipGetLastError();
 }
 
@@ -214,8 +219,10 @@ hipError_t argmax_rows(const float* logits, int32_t* next, int rows, int cols, h
   return hipGetLastError();
 }
 
-template hipError_t rmsnorm<bf16>(const bf16*, int64_t, const bf16*, bf16*, int64_t, int, float, hipStream_t);
-template hipError_t rmsnorm<float>(const float*, int64_t, const float*, float*, int64_t, int, float, hipStream_t);
+template hipError_t rmsnorm<bf16>(const bf16*, int64_t, const bf16*, bf16*, int64_t, int, float, hipStream_t,
+                                  float*);
+template hipError_t rmsnorm<float>(const float*, int64_t, const float*, float*, int64_t, int, float, hipStream_t,
+                                   float*);
 template hipError_t rope_apply<bf16>(bf16*, const float*, int, int, int, int, int, hipStream_t);
 template hipError_t rope_apply<float>(float*, const float*, int, int, int, int, int, hipStream_t);
 template hipError_t embedding<bf16>(const int32_t*, const bf16*, bf16*, int64_t, int, int, hipStream_t);

@@ -6,9 +6,11 @@
 
 namespace llama {
 
+// y = RMSNorm(x) * w.  With rscale != nullptr: y = x * w and rscale[row] =
+// rsqrt(mean(x^2) + eps), for a projection that scales its accumulators.
 template <typename T>
 hipError_t rmsnorm(const T* x, int64_t x_stride, const T* w, T* y, int64_t rows, int dim, float eps,
-                   hipStream_t st);
+                   hipStream_t st, float* rscale = nullptr);
 
 hipError_t rope_table(float* freqs, int head_dim, int end, double theta, hipStream_t st);
 

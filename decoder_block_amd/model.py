@@ -1,0 +1,94 @@
+"""Whole-model greedy generation on one GPU through the C ABI.
+
+Token embedding -> n_layers x llama_block_forward -> final RMSNorm + output
+projection of the last position -> argmax, with the greedy token written on
+the device and fed straight back as the next call's input (no host round trip
+per token).  Follows the linkmax.top walkthrough of Meta's LLaMA code,
+section 3.2.2 (Transformer.forward: embedding, layers, norm, output on the last
+position) and section 3.3 (generate: one prefill call, then one-token calls at
+the previous position; argmax when the temperature is 0).
+
+torch only allocates device memory and provides the stream; every step of the
+forward pass runs in the HIP library.
+"""
+from __future__ import annotations
+
+from typing import Callable, Dict, List, Optional
+
+import torch
+
+from . import _lib as L
+from .runner import BlockRunner
+
+
+class StackRunner:
+    def __init__(self, args: L.ModelArgs, layer_weights: Callable[[int], Dict[str, torch.Tensor]],
+                 embedding: torch.Tensor, norm_w: torch.Tensor, w_out: torch.Tensor, dtype=torch.bfloat16,
+                 device="cuda:0"):
+        """``layer_weights(l)`` returns layer l's tensors (CPU or device); they are moved
+        to the device one layer at a time."""
+        self.args = args
+        self.dtype = dtype
+        self.ldt = L.LLAMA_BF16 if dtype == torch.bfloat16 else L.LLAMA_F32
+        self.device = torch.device(device)
+        self.layers: List[BlockRunner] = []
+        freqs = None
+        for l in range(args.n_layers):
+            r = BlockRunner(args, layer_weights(l), dtype, self.device, share_freqs=freqs)
+            freqs = (r.freqs, r.freqs_end)
+            self.layers.append(r)
+        self.embedding = embedding.to(self.device, dtype)
+        self.norm_w = norm_w.to(self.device, dtype)
+        self.w_out = w_out.to(self.device, dtype)
+        self.vocab = self.w_out.shape[0]
+        self.ws: Optional[torch.Tensor] = None
+        self.bufs: Optional[List[torch.Tensor]] = None
+
+    def _workspace(self, bsz: int, seqlen: int, start_pos: int) -> int:
+        need = L.llama_block_workspace_size(self.args, bsz, seqlen, start_pos, self.ldt)
+        need = max(need, L.llama_lm_head_workspace_size(bsz, self.args.dim, self.vocab, self.ldt))
+        if self.ws is None or self.ws.numel() < need:
+            self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self.ws.numel()
+
+    def _acts(self, bsz: int, seqlen: int) -> List[torch.Tensor]:
+        n = bsz * seqlen * self.args.dim
+        if self.bufs is None or self.bufs[0].numel() < n:
+            self.bufs = [torch.empty(n, dtype=self.dtype, device=self.device) for _ in range(2)]
+        return [b[:n].view(bsz, seqlen, self.args.dim) for b in self.bufs]
+
+    def forward(self, tokens: torch.Tensor, start_pos: int, logits: torch.Tensor, next_tok: torch.Tensor,
+                layer_hook=None) -> None:
+        """One call (prefill when tokens has several columns, decode when one):
+        writes the last position's fp32 logits [bsz, vocab] and greedy ids [bsz]."""
+        bsz, seqlen = tokens.shape
+        ws_bytes = self._workspace(bsz, seqlen, start_pos)
+        a, b = self._acts(bsz, seqlen)
+        D = self.args.dim
+        L.llama_embedding(tokens, self.embedding, a, bsz * seqlen, D, self.vocab)
+        for i, layer in enumerate(self.layers):
+            L.llama_block_forward(self.args, layer.cw, layer.cache_k, layer.cache_v, layer.freqs, layer.freqs_end,
+                                  a, b, bsz, seqlen, start_pos, self.ws, ws_bytes)
+            if layer_hook is not None:
+                layer_hook(i, a, b)
+            a, b = b, a
+        last = a[:, seqlen - 1]                # row stride seqlen * dim
+        L.llama_lm_head_argmax(last, seqlen * D, self.norm_w, self.w_out, logits, next_tok, bsz, D, self.vocab,
+                               self.args.norm_eps, self.ws, ws_bytes)
+
+    def generate(self, prompt: torch.Tensor, steps: int, on_step=None) -> torch.Tensor:
+        """Greedy generation: prefill the prompt, then ``steps`` one-token calls.
+        Returns the generated ids [steps + 1, bsz]: row t is the device-side argmax
+        of call t and is passed, as is, as the input ids of call t + 1 (no host
+        synchronisation inside the loop)."""
+        bsz, S = prompt.shape
+        out = torch.empty(steps + 1, bsz, dtype=torch.int32, device=self.device)
+        logits = torch.empty(bsz, self.vocab, dtype=torch.float32, device=self.device)
+        self.forward(prompt, 0, logits, out[0])
+        if on_step is not None:
+            on_step(0, logits, out[0])
+        for t in range(steps):
+            self.forward(out[t].view(bsz, 1), S + t, logits, out[t + 1])
+            if on_step is not None:
+                on_step(t + 1, logits, out[t + 1])
+        return out

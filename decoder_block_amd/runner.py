@@ -16,7 +16,7 @@ from . import _lib as L
 
 class BlockRunner:
     def __init__(self, args: L.ModelArgs, weights: Dict[str, torch.Tensor], dtype: torch.dtype,
-                 device="cuda:0", cache=None):
+                 device="cuda:0", cache=None, share_freqs=None):
         self.args = args
         self.dtype = dtype
         self.ldt = L.LLAMA_BF16 if dtype == torch.bfloat16 else L.LLAMA_F32
@@ -31,9 +31,14 @@ class BlockRunner:
             self.cache_v = torch.zeros(shape, dtype=dtype, device=self.device)
         else:
             self.cache_k, self.cache_v = (c.to(self.device, dtype) for c in cache)
-        self.freqs_end = 2 * args.max_seq_len
-        self.freqs = torch.empty(self.freqs_end, self.head_dim // 2, 2, dtype=torch.float32, device=self.device)
-        L.llama_rope_freqs(self.freqs, self.head_dim, self.freqs_end, args.rope_theta)
+        if share_freqs is not None:
+            self.freqs, self.freqs_end = share_freqs
+        else:
+            # the table spans 2 * max_seq_len positions, as precompute_freqs_cis is called
+            self.freqs_end = 2 * args.max_seq_len
+            self.freqs = torch.empty(self.freqs_end, self.head_dim // 2, 2, dtype=torch.float32,
+                                     device=self.device)
+            L.llama_rope_freqs(self.freqs, self.head_dim, self.freqs_end, args.rope_theta)
         self.ws: Optional[torch.Tensor] = None
 
     def workspace(self, bsz: int, seqlen: int, start_pos: int) -> int:

@@ -1,0 +1,112 @@
+"""The 32-layer Llama-3-8B-shaped stack (embedding, 32 blocks, final RMSNorm,
+output projection of the last position, greedy argmax fed back on the device).
+
+Parity is checked layer by layer at the stack's shapes with the oracle driving
+every input: the oracle runs its own float64 chain through all 32 layers on a
+prompt prefix (and one decode step), and each GPU layer receives the oracle's
+layer input (rounded to bf16) and is compared with the oracle's layer output.
+No GPU result is fed to the oracle.  The full workload (batch 64 x 2048-token
+prompts, 256 greedy steps) then runs end to end on the GPU, where the greedy
+feedback is checked exactly against each step's logits.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from decoder_block_amd import _lib as L
+from decoder_block_amd.model import StackRunner
+from decoder_block_amd.runner import model_args_for
+from oracle import block as ob
+from tests.gpu_util import check, errors, f64, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+W5 = wl.WORKLOADS[5]
+
+
+@pytest.fixture(scope="module")
+def host_weights():
+    print(f"case {W5.name}: generating {W5.n_layers} layers of seeded weights", flush=True)
+    layers = [wl.block_weights(W5, l) for l in range(W5.n_layers)]
+    emb, norm_w, w_out = wl.stack_tensors(W5)
+    return layers, emb, norm_w, w_out
+
+
+def _bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16)
+
+
+def test_stack_layers_follow_the_oracle_chain(host_weights):
+    dev = need_gpu()
+    layers, emb, norm_w, w_out = host_weights
+    P = 96                                   # prompt prefix evaluated by the oracle
+    w = W5
+    print(f"case {w.name}: oracle-driven per-layer parity, prefix {P} + 1 decode step", flush=True)
+    args = model_args_for(w, max_batch=1, max_seq=P + 1)
+    stack = StackRunner(args, lambda l: layers[l], emb, norm_w, w_out, torch.bfloat16, dev)
+    prompt = wl.prompt_tokens(w)[:1, :P + 1]         # row 0; token P is the decode-step input
+    tok = prompt.numpy()
+    # oracle chain (float64) from the embedding rows
+    h = f64(emb)[tok[:, :P]]
+    hd = f64(emb)[tok[:, P:P + 1]]
+    worst = 0.0
+    shape = (1, P + 1, w.n_kv_heads, w.head_dim)
+    for l in range(w.n_layers):
+        W = {k: v.to(torch.float64).numpy() for k, v in layers[l].items()}
+        ck, cv = np.zeros(shape), np.zeros(shape)
+        h_next = ob.block_forward(h, W, ck, cv, 0, w.n_heads, w.n_kv_heads, w.norm_eps, w.rope_theta)
+        hd_next = ob.block_forward(hd, W, ck, cv, P, w.n_heads, w.n_kv_heads, w.norm_eps, w.rope_theta)
+        r = stack.layers[l]
+        got = r.forward(_bf16(h).to(dev), 0)
+        got_d = r.forward(_bf16(hd).to(dev), P)
+        torch.cuda.synchronize()
+        e = check(got, h_next, "bf16", f"layer {l} prefill")
+        ed = check(got_d, hd_next, "bf16", f"layer {l} decode step")
+        worst = max(worst, e["relf"], ed["relf"])
+        h, hd = h_next, hd_next
+    print(f"[parity] worst per-layer relF {worst:.3e}", flush=True)
+    # final RMSNorm + output projection + greedy token from the oracle's last hidden state
+    for name, last in (("prefill", h[:, -1]), ("decode", hd[:, -1])):
+        ref = ob.linear(ob.rms_norm(last, f64(norm_w), w.norm_eps), f64(w_out))
+        logits = torch.empty(1, w.vocab_size, dtype=torch.float32, device=dev)
+        nxt = torch.empty(1, dtype=torch.int32, device=dev)
+        nb = L.llama_lm_head_workspace_size(1, w.dim, w.vocab_size, L.LLAMA_BF16)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        L.llama_lm_head_argmax(_bf16(last).to(dev), w.dim, stack.norm_w, stack.w_out, logits, nxt, 1, w.dim,
+                               w.vocab_size, w.norm_eps, ws, nb)
+        torch.cuda.synchronize()
+        e = check(logits, ref, "bf16", f"{name} logits")
+        g = int(nxt.item())
+        lg = f64(logits)[0]
+        assert g == int(np.argmax(lg))                               # exact on the GPU's logits
+        assert ref[0, g] >= ref[0].max() - 2 * e["raw_maxabs"]        # a correct greedy token
+
+
+def test_stack_full_workload_greedy_generation(host_weights):
+    dev = need_gpu()
+    layers, emb, norm_w, w_out = host_weights
+    w = W5
+    steps = w.decode_steps
+    print(f"case {w.name}: B={w.batch} prompt {w.prefill_len} + {steps} greedy steps", flush=True)
+    stack = StackRunner(model_args_for(w), lambda l: layers[l], emb, norm_w, w_out, torch.bfloat16, dev)
+    prompt = wl.prompt_tokens(w).to(dev)
+    checked = {}
+
+    def on_step(t, logits, nxt):
+        if t in (0, 1, steps // 2, steps):
+            checked[t] = (f64(logits), nxt.cpu().numpy().copy())
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    out = stack.generate(prompt, steps, on_step)
+    ev[1].record()
+    torch.cuda.synchronize()
+    print(f"[stack] prefill + {steps} steps: {ev[0].elapsed_time(ev[1]):.1f} ms (includes host checks)", flush=True)
+    ids = out.cpu().numpy()
+    assert ids.shape == (steps + 1, w.batch)
+    assert ids.min() >= 0 and ids.max() < w.vocab_size
+    for t, (lg, nxt) in checked.items():
+        assert np.all(np.isfinite(lg))
+        np.testing.assert_array_equal(nxt, np.argmax(lg, axis=1))   # greedy = argmax, lowest id on ties
+        np.testing.assert_array_equal(ids[t], nxt)                   # and that id was fed to the next call

@@ -147,3 +147,15 @@ def prefilled_cache(w: Workload, layer: int = 0) -> Tuple[torch.Tensor, torch.Te
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact upcast of a (bf16 or f32) tensor to a float64 numpy array."""
     return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def stack_tensors(w: Workload):
+    """Embedding [vocab, dim], final RMSNorm weight (ones) and output projection [vocab, dim]."""
+    emb = normal((w.vocab_size, w.dim), WEIGHT_STD, w.dtype, w.wid, 0, T_EMBED)
+    out = normal((w.vocab_size, w.dim), WEIGHT_STD, w.dtype, w.wid, 0, T_OUTPUT)
+    return emb, torch.ones(w.dim, dtype=torch_dtype(w.dtype)), out
+
+
+def prompt_tokens(w: Workload) -> torch.Tensor:
+    """Random prompt ids [batch, prefill_len], uniform over the vocabulary."""
+    return tokens((w.batch, w.prefill_len), w.vocab_size, w.wid)
