@@ -11,11 +11,12 @@
 // Prefill (bf16): one workgroup owns 128 query rows = G heads of one kv group
 // x 128/G positions, so each K/V tile is staged in LDS once and used by all G
 // heads (GQA sharing).  Key tiles entirely above the causal diagonal of the
-// block are never loaded.  S^T = K.Q^T and O^T = V^T.P^T on
-// v_mfma_f32_32x32x16_bf16 put one query row per lane column, so the row
-// max/sum need one cross-half exchange only, and the probabilities feed the
-// second MFMA straight from registers (keys are permuted in the V^T tile to
-// match the accumulator layout).
+// block are never loaded, and the mask is evaluated only on tiles that meet
+// the diagonal.  S^T = K.Q^T and O^T = V^T.P^T on v_mfma_f32_32x32x16_bf16 put
+// one query row per lane column, so the row max/sum need one cross-half
+// exchange only, and the probabilities feed the second MFMA straight from
+// registers (the V^T operand is read with transposing LDS loads whose key
+// order matches the accumulator layout).
 //
 // Decode (bf16): split-K over keys.  Each wave streams chunks of 32 keys from
 // HBM (K straight into MFMA operand registers, V through a wave-private
@@ -94,20 +95,35 @@ __global__ void __launch_bounds__(256) attn_simple(const T* __restrict__ q, cons
 }
 
 // ------------------------------------------------------------------ prefill (bf16 MFMA)
+#define LLAMA_LDS __attribute__((address_space(3)))
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+template <int N>
+__device__ __forceinline__ void attn_wait_vmcnt() {
+  // s_waitcnt simm16 on gfx9: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// K and V tiles of 64 keys are copied global -> LDS by global_load_lds_dwordx4
+// in their natural [key][d] layout (2-slot ring), 16-byte chunks XOR-swizzled
+// per key.  Q.K^T reads K fragments with ds_read_b128; the P.V product needs
+// V^T fragments (8 keys of one d per lane), which ds_read_b64_tr_b16 delivers
+// from the natural layout: within each 16-lane group, lane i receives element i
+// of the 16-element rows read by lanes 4r..4r+3, r = 0..3 (four keys).
 template <int HD>
 __global__ void __launch_bounds__(256, 2)
 attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const bf16* __restrict__ cv,
                   bf16* __restrict__ out, AttnShape sh, int G, float scale_log2) {
   constexpr int BKV = 64;
-  constexpr int CHK = HD / 8;                 // 16-byte chunks per K row
-  constexpr int KL = BKV * CHK / 256;         // K chunks per thread per tile
-  constexpr int VT = 16 * CHK;                // V transpose tasks (4 keys x 8 d each)
+  constexpr int CHK = HD / 8;                 // 16-byte chunks per key row
+  constexpr int KPB = 1024 / (HD * 2);        // key rows per 1 KiB DMA block
+  constexpr int DMA = BKV / KPB / 4;          // DMA instructions per wave per tensor per tile
   static_assert(HD == 64 || HD == 128, "head_dim");
-  // XOR swizzles: the 16 lanes of a ds_read_b128 phase (16 consecutive rows, one
-  // chunk) land on 16 distinct 16-byte bank groups of the 64-bank LDS
-  __shared__ bf16x8 Ks[2][BKV * CHK];         // [key][chunk ^ f(key)]
-  __shared__ bf16x8 Vt[2][HD * (BKV / 8)];    // [d][key chunk ^ ((d >> 1) & 7)], keys permuted
-  auto kswz = [](int key, int c) { return CHK == 16 ? (c ^ (key & 15)) : (c ^ ((key >> 1) & 7)); };
+  __shared__ bf16x8 Ks[2][BKV * CHK];
+  __shared__ bf16x8 Vs[2][BKV * CHK];
+  // bank-group swizzles: K rows are read 16 keys at a time (one chunk), V rows 4 keys x 32 bytes
+  auto kswz = [](int key) { return CHK == 16 ? (key & 15) : ((key >> 1) & 7); };
+  auto vswz = [](int key) { return CHK == 16 ? ((key & 3) << 2) : (((key >> 1) & 1) << 2); };
 
   const int H = sh.n_heads, Hkv = sh.n_kv_heads, S = sh.seqlen, p0 = sh.start_pos;
   const int n_rep = H / Hkv;
@@ -129,6 +145,7 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
   const bool row_valid = s < S;
   const int s_c = row_valid ? s : S - 1;
   const int qpos = p0 + s;
+  const int wave_qmin = p0 + qb * BQ + (wave * 32) % BQ;   // smallest query position of this wave
 
   bf16x8 qf[HD / 16];
   {
@@ -144,43 +161,20 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
   const bf16* kbase = ck + ((int64_t)b * sh.max_seq * Hkv + j) * HD;
   const bf16* vbase = cv + ((int64_t)b * sh.max_seq * Hkv + j) * HD;
 
-  bf16x8 kreg[KL], vreg[4];
-  auto gload = [&](int t0) {
+  // DMA of key tile t0 into ring slot st: block (wave*DMA + i) holds keys
+  // KPB*(wave*DMA + i) .. +KPB; lane l fetches key + l/CHK, chunk (l%CHK) ^ swz(key)
+  auto issue = [&](int t0, int st) {
 #pragma unroll
-    for (int i = 0; i < KL; ++i) {
-      int key = t0 + tid / CHK + i * (256 / CHK);
-      int c = tid % CHK;
-      kreg[i] = key < kend ? *(const bf16x8*)(kbase + key * stride + c * 8) : bf16x8{};
-    }
-    if (tid < VT) {
-      int kg = tid / CHK, c = tid % CHK;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        int key = t0 + kg * 4 + e;
-        vreg[e] = key < kend ? *(const bf16x8*)(vbase + key * stride + c * 8) : bf16x8{};
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KL; ++i) {
-      int key = tid / CHK + i * (256 / CHK);
-      int c = tid % CHK;
-      Ks[buf][key * CHK + kswz(key, c)] = kreg[i];
-    }
-    if (tid < VT) {
-      int kg = tid / CHK, dc = tid % CHK;
-      int g4 = kg & 3;
-      int g4p = (g4 == 1) ? 2 : (g4 == 2 ? 1 : g4);   // swap the middle 4-key groups
-      int pos = (kg >> 2) * 16 + g4p * 4;
-      int pc = pos >> 3, off = pos & 7;
-#pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8) {
-        int d = dc * 8 + e8;
-        bf16x4 v4 = {vreg[0][e8], vreg[1][e8], vreg[2][e8], vreg[3][e8]};
-        bf16* rowp = (bf16*)&Vt[buf][d * 8 + (pc ^ ((d >> 1) & 7))];
-        *(bf16x4*)(rowp + off) = v4;
-      }
+    for (int i = 0; i < DMA; ++i) {
+      const int blk = wave * DMA + i;
+      const int key = blk * KPB + lane / CHK;
+      const int t = min(t0 + key, kend - 1);
+      const int ckk = (lane % CHK) ^ kswz(key);
+      const int cvv = (lane % CHK) ^ vswz(key);
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + t * stride + ckk * 8),
+                                       (LLAMA_LDS void*)&Ks[st][blk * 64], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vbase + t * stride + cvv * 8),
+                                       (LLAMA_LDS void*)&Vs[st][blk * 64], 16, 0, 0);
     }
   };
 
@@ -188,15 +182,19 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
 #pragma unroll
   for (int i = 0; i < HD / 32; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
+  // V^T read: lane group g = lane/16 covers d0 = (g&1)*16 (+32*dt), keys base + hf*4 (+8)
+  const int li = lane & 15;
+  const int vkey_off = lhalf * 4 + (li >> 2);
+  const int vd_off = ((lane >> 4) & 1) * 16 + (li & 3) * 4;
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
+  issue(0, 0);
   for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
+    const int st = it & 1;
     const int t0 = it * BKV;
-    if (it + 1 < ntiles) gload(t0 + BKV);
+    attn_wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (it + 1 < ntiles) issue(t0 + BKV, st ^ 1);
 
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
@@ -205,57 +203,68 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
 #pragma unroll
       for (int kk = 0; kk < HD / 16; ++kk) {
         const int c = kk * 2 + lhalf;
-        bf16x8 kf = Ks[buf][key * CHK + kswz(key, c)];
+        const bf16x8 kf = Ks[st][key * CHK + (c ^ kswz(key))];
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[kt], 0, 0, 0);
       }
     }
-    // scale, causal mask, row max (lane holds 32 of the row's 64 keys; lane^32 the rest)
-    float mloc = -INFINITY;
+    // causal mask only where this wave's rows meet the diagonal
+    if (t0 + BKV - 1 > wave_qmin) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int t = t0 + kt * 32 + (v >> 2) * 8 + lhalf * 4 + (v & 3);
+          if (t > qpos) sacc[kt][v] = -INFINITY;
+        }
+    }
+    float mraw = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        int t = t0 + kt * 32 + (v >> 2) * 8 + lhalf * 4 + (v & 3);
-        float x = sacc[kt][v] * scale_log2;
-        x = (t > qpos) ? -INFINITY : x;
-        sacc[kt][v] = x;
-        mloc = fmaxf(mloc, x);
-      }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = exp2f(m_run - m_new);
+      for (int v = 0; v < 16; ++v) mraw = fmaxf(mraw, sacc[kt][v]);
+    mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+    const float mt = mraw * scale_log2;       // tile max in the log2 domain (scale > 0)
+    // lazy rescale: the running max moves only when some row's max grows by more
+    // than 8 (probabilities then stay below 2^8); the result is unchanged
+    if (__any(mt > m_run + 8.0f)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < HD / 32; ++dt) oacc[dt] *= alpha;
+      m_run = m_new;
+    }
     float psum = 0.f;
+    bf16x8 pf[2][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        float p = exp2f(sacc[kt][v] - m_new);
-        sacc[kt][v] = p;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][v], scale_log2, -m_run));
         psum += p;
+        pf[kt][v >> 3][v & 7] = (bf16)p;
       }
     psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < HD / 32; ++dt) oacc[dt] *= alpha;
+    l_run += psum;
 
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        bf16x8 pf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[e] = (bf16)sacc[kt][h2 * 8 + e];
-        const int pc = kt * 4 + h2 * 2 + lhalf;
+        const int key0 = kt * 32 + h2 * 16 + vkey_off;
 #pragma unroll
         for (int dt = 0; dt < HD / 32; ++dt) {
-          const int d = dt * 32 + lrow;
-          bf16x8 vf = Vt[buf][d * 8 + (pc ^ ((d >> 1) & 7))];
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[dt], 0, 0, 0);
+          const int d = dt * 32 + vd_off;
+          const int k1 = key0, k2 = key0 + 8;
+          const bf16* v1 = (const bf16*)&Vs[st][k1 * CHK + ((d >> 3) ^ vswz(k1))] + (d & 7);
+          const bf16* v2 = (const bf16*)&Vs[st][k2 * CHK + ((d >> 3) ^ vswz(k2))] + (d & 7);
+          const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LLAMA_LDS bf16x4_t*)v1);
+          const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LLAMA_LDS bf16x4_t*)v2);
+          const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kt][h2], oacc[dt], 0, 0, 0);
         }
       }
-    if (it + 1 < ntiles) sstore(buf ^ 1);
-    __syncthreads();
+    asm volatile("" ::: "memory");
   }
 
   if (!row_valid) return;
