@@ -446,22 +446,53 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
   }
 }
 
+// Log-sum-exp merge of the split partials of one (b, head): 256 threads, the
+// splits spread over the threads (no serial walk over the splits).
 template <typename T>
-__global__ void attn_decode_combine(const float* __restrict__ partial, T* __restrict__ out, int nsplit,
-                                    int HD) {
+__global__ void __launch_bounds__(256)
+attn_decode_combine(const float* __restrict__ partial, T* __restrict__ out, int nsplit, int HD) {
+  __shared__ float red[256];
+  __shared__ float wz[1024];
   const int64_t bh = blockIdx.x;
-  const int d = threadIdx.x;
+  const int t = threadIdx.x;
   const float* base = partial + bh * nsplit * (HD + 2);
+  // 1) global max of the split maxima
   float M = -INFINITY;
-  for (int z = 0; z < nsplit; ++z) M = fmaxf(M, base[z * (HD + 2) + HD]);
-  float acc = 0.f, Ls = 0.f;
-  for (int z = 0; z < nsplit; ++z) {
+  for (int z = t; z < nsplit; z += 256) M = fmaxf(M, base[z * (HD + 2) + HD]);
+  M = wave_max(M);
+  if ((t & 63) == 0) red[t >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  // 2) split weights and the total sum
+  float Ls = 0.f;
+  for (int z = t; z < nsplit; z += 256) {
     const float* p = base + z * (HD + 2);
-    float w = p[HD] == -INFINITY ? 0.f : exp2f(p[HD] - M);
+    const float w = p[HD] == -INFINITY ? 0.f : exp2f(p[HD] - M);
+    if (z < 1024) wz[z] = w;
     Ls += w * p[HD + 1];
+  }
+  Ls = wave_sum(Ls);
+  if ((t & 63) == 0) red[t >> 6] = Ls;
+  __syncthreads();
+  Ls = red[0] + red[1] + red[2] + red[3];
+  // 3) weighted sum of the partial outputs: thread (d, zs) sums splits zs, zs+R, ...
+  const int R = 256 / HD;
+  const int d = t % HD, zs = t / HD;
+  float acc = 0.f;
+#pragma unroll 8
+  for (int z = zs; z < nsplit; z += R) {
+    const float* p = base + z * (HD + 2);
+    const float w = z < 1024 ? wz[z] : (p[HD] == -INFINITY ? 0.f : exp2f(p[HD] - M));
     acc += w * p[d];
   }
-  out[bh * HD + d] = from_f<T>(acc / Ls);
+  __syncthreads();
+  red[t] = acc;
+  __syncthreads();
+  if (zs == 0) {
+    for (int r = 1; r < R; ++r) acc += red[r * HD + d];
+    out[bh * HD + d] = from_f<T>(acc / Ls);
+  }
 }
 
 }  // namespace
@@ -530,7 +561,7 @@ hipError_t attn_decode(const T* q, const T* cache_k, const T* cache_v, T* out, c
       attn_decode_mfma<64><<<grid, 256, 0, st>>>(q, cache_k, cache_v, out, partial, sh, ns, L, scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1) return e;
-    attn_decode_combine<T><<<sh.bsz * sh.n_heads, sh.head_dim, 0, st>>>(partial, out, ns, sh.head_dim);
+    attn_decode_combine<T><<<sh.bsz * sh.n_heads, 256, 0, st>>>(partial, out, ns, sh.head_dim);
   } else {
     const int64_t waves = (int64_t)sh.bsz * sh.n_heads;
     attn_simple<T><<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(q, cache_k, cache_v, out, sh, scale);

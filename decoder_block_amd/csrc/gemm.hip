@@ -19,7 +19,9 @@ namespace llama {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kStages = 4;   // LDS ring depth of the DMA-pipelined kernel
+constexpr int kStages = 4;        // LDS ring depth of the DMA-pipelined kernel, large M (BK = 32)
+constexpr int kSkinnyBK = 64;     // small M: 128-byte row pieces per k-tile
+constexpr int kSkinnyStages = 3;  // small M: ring depth (3 x 40 KiB)
 
 template <typename T>
 __device__ __forceinline__ const T* weight_row(const WeightRows<T>& w, int n, int K) {
@@ -235,34 +237,46 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(63 | (7 << 4) | (0 << 8) | (3 << 14)); }
 
-template <int NS, bool DUAL, class Epi>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M, int N, int K, Epi epi) {
-  constexpr int BM = 256, BN = 256, BK = 32, CH = 4;
-  constexpr int WM = 128, WN = 128, TM = 4, TN = 4;
-  constexpr int ROWS = BM + BN;               // 512 rows x 64 B = 32 KiB per stage
-  constexpr int BLOCKS = ROWS / 16;           // 1 KiB DMA blocks per stage
+template <int BM, int BN, int BK, int WAVES_M, int NS, bool DUAL, bool SPLIT, class Epi>
+__global__ void __launch_bounds__(kThreads)
+gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M, int N, int K, int k_per_split,
+              Epi epi, float* __restrict__ partial) {
+  constexpr int CH = BK / 8;                  // 16-byte chunks per tile row
+  constexpr int RPB = 64 / CH;                // tile rows per 1 KiB DMA block
+  constexpr int WAVES_N = 4 / WAVES_M;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int ROWS = BM + BN;               // rows x 2*BK bytes per stage
+  constexpr int BLOCKS = ROWS / RPB;          // 1 KiB DMA blocks per stage
   constexpr int LOADS = BLOCKS / 4;           // per wave (and per lane) per stage
   constexpr int BN_OUT = DUAL ? BN / 2 : BN;
-  static_assert(NS >= 3, "ring depth");
+  constexpr int RD = TN + TM;                 // fragment reads per 16-deep half
+  constexpr int MF = TN * TM;                 // MFMAs per half
+  static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(NS >= 2 && BLOCKS % 4 == 0 && TM >= 1 && TN >= 1 && (!DUAL || TN % 2 == 0), "shape");
+  static_assert(MF % RD == 0, "interleave");
   __shared__ bf16x8 smem[NS][ROWS * CH];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (N + BN_OUT - 1) / BN_OUT;
   int tm, tn;
   tile_coords(tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN_OUT;
-  const int nk = K / BK;
+  const int kb = blockIdx.z * k_per_split;
+  const int nk = (min(K, kb + k_per_split) - kb) / BK;
 
+  // bank-group swizzle of the 16-byte chunks: a ds_read_b128 phase reads one
+  // chunk of 16 consecutive rows, which must hit 16 distinct bank groups
+  auto swz = [](int r) { return BK == 32 ? ((r >> 2) & 3) : ((r >> 1) & 7); };
   // this lane's source row pointer (+ chunk offset) for each of its DMA blocks
   const bf16* src[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int blk = wave * LOADS + i;
-    const int r = blk * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((lane >> 4) & 3);
+    const int r = blk * RPB + lane / CH;
+    const int c = (lane % CH) ^ swz(r);
     const bf16* p;
     if (r < BM) {
       p = A + (int64_t)min(m0 + r, M - 1) * lda;
@@ -275,7 +289,7 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
         p = weight_row(w, min(n0 + rb, N - 1), K);
       }
     }
-    src[i] = p + c * 8;
+    src[i] = p + kb + c * 8;
   }
   // DMA of k-tile kt into ring slot kt % NS (kt is clamped to the last tile so the
   // refill at the end of the loop stays branch-free; those copies are never read)
@@ -298,12 +312,12 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       const int r = BM + wrow(t) + lrow;
-      fa[t] = smem[st][r * CH + (c ^ ((r >> 2) & 3))];
+      fa[t] = smem[st][r * CH + (c ^ swz(r))];
     }
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
       const int r = wm * WM + t * 32 + lrow;
-      fb[t] = smem[st][r * CH + (c ^ ((r >> 2) & 3))];
+      fb[t] = smem[st][r * CH + (c ^ swz(r))];
     }
   };
 
@@ -319,43 +333,50 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
       for (int b = 0; b < TM; ++b)
         acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
   };
-  // 8 fragment reads spread over 16 MFMAs
+  // RD fragment reads spread over MF MFMAs
   auto interleave = [&]() {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    for (int i = 0; i < RD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, MF / RD, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
 
-  bf16x8 fa0[TN], fb0[TM], fa1[TN], fb1[TM];
+  constexpr int KS = BK / 16;                 // 16-deep MFMA steps per k-tile
+  bf16x8 fa[2][TN], fb[2][TM];
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) issue(s);
   wait_vmcnt<(NS - 2) * LOADS>();
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   issue(NS - 1);
-  read_half(0, 0, fa0, fb0);
+  read_half(0, 0, fa[0], fb[0]);
 
   for (int kt = 0; kt < nk - 1; ++kt) {
     const int st = kt % NS;
-    read_half(st, 1, fa1, fb1);
-    mfma_half(fa0, fb0);
-    interleave();
+#pragma unroll
+    for (int ks = 0; ks < KS - 1; ++ks) {
+      read_half(st, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      mfma_half(fa[ks & 1], fb[ks & 1]);
+      interleave();
+    }
     // tile kt+1 landed (NS-2 later tiles may still be in flight); our reads of slot st are done
     wait_vmcnt<(NS - 2) * LOADS>();
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     issue(kt + NS);
-    read_half((kt + 1) % NS, 0, fa0, fb0);
-    mfma_half(fa1, fb1);
+    read_half((kt + 1) % NS, 0, fa[KS & 1], fb[KS & 1]);
+    mfma_half(fa[(KS - 1) & 1], fb[(KS - 1) & 1]);
     interleave();
   }
-  read_half((nk - 1) % NS, 1, fa1, fb1);
-  mfma_half(fa0, fb0);
-  interleave();
-  mfma_half(fa1, fb1);
+#pragma unroll
+  for (int ks = 0; ks < KS - 1; ++ks) {
+    read_half((nk - 1) % NS, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+    mfma_half(fa[ks & 1], fb[ks & 1]);
+    interleave();
+  }
+  mfma_half(fa[(KS - 1) & 1], fb[(KS - 1) & 1]);
   // no DMA may still be writing LDS when the workgroup retires
   wait_vmcnt<0>();
 
@@ -373,7 +394,13 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
           f32x4 v1 = {acc[a][b][g * 4], acc[a][b][g * 4 + 1], acc[a][b][g * 4 + 2], acc[a][b][g * 4 + 3]};
           const f32x16& a3 = acc[a + TN / 2][b];
           f32x4 v3 = {a3[g * 4], a3[g * 4 + 1], a3[g * 4 + 2], a3[g * 4 + 3]};
-          epi(m, n, v1, v3);
+          if (SPLIT) {
+            float* p = partial + ((int64_t)blockIdx.z * M + m) * (2 * (int64_t)N);
+            *(f32x4*)(p + n) = v1;
+            *(f32x4*)(p + N + n) = v3;
+          } else {
+            epi(m, n, v1, v3);
+          }
         }
     } else {
 #pragma unroll
@@ -383,7 +410,10 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
           const int n = n0 + wn * WN + a * 32 + g * 8 + lhalf * 4;
           if (n >= N) continue;
           f32x4 v = {acc[a][b][g * 4], acc[a][b][g * 4 + 1], acc[a][b][g * 4 + 2], acc[a][b][g * 4 + 3]};
-          epi(m, n, v);
+          if (SPLIT)
+            *(f32x4*)(partial + ((int64_t)blockIdx.z * M + m) * (int64_t)N + n) = v;
+          else
+            epi(m, n, v);
         }
     }
   }
@@ -465,30 +495,77 @@ gemm_f32_fma(const float* __restrict__ A, int64_t lda, WeightRows<float> w, int 
 }
 
 // ------------------------------------------------------------------ split-K reduce
-template <bool DUAL, class Epi>
+// Z lanes share one output group (4 columns of one row): lane z sums the splits
+// z, z+Z, ... (independent loads in flight), xor-shuffles combine the Z partial
+// sums and lane 0 applies the epilogue.  Z = 8 when there are few groups (one
+// token: the latency of the split walk dominates), 1 otherwise.
+template <bool DUAL, int Z, class Epi>
 __global__ void __launch_bounds__(kThreads)
 splitk_reduce(const float* __restrict__ partial, int splits, int M, int N, Epi epi) {
   const int64_t groups = (int64_t)M * (N / 4);
-  for (int64_t gi = (int64_t)blockIdx.x * kThreads + threadIdx.x; gi < groups;
-       gi += (int64_t)gridDim.x * kThreads) {
-    int m = (int)(gi / (N / 4));
-    int n = (int)(gi % (N / 4)) * 4;
+  const int zl = threadIdx.x % Z;
+  for (int64_t gi = ((int64_t)blockIdx.x * kThreads + threadIdx.x) / Z; gi < groups;
+       gi += (int64_t)gridDim.x * (kThreads / Z)) {
+    const int m = (int)(gi / (N / 4));
+    const int n = (int)(gi % (N / 4)) * 4;
     const int64_t row = DUAL ? 2 * (int64_t)N : (int64_t)N;
     const int64_t stride = (int64_t)M * row;
-    f32x4 s = {}, s3 = {};
     const float* p = partial + (int64_t)m * row + n;
-    for (int z = 0; z < splits; ++z) {
+    f32x4 s = {}, s3 = {};
+#pragma unroll 4
+    for (int z = zl; z < splits; z += Z) {
       s += *(const f32x4*)(p + z * stride);
       if (DUAL) s3 += *(const f32x4*)(p + z * stride + N);
     }
-    if constexpr (DUAL)
-      epi(m, n, s, s3);
-    else
-      epi(m, n, s);
+#pragma unroll
+    for (int off = 1; off < Z; off <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[i] += __shfl_xor(s[i], off, 64);
+        if (DUAL) s3[i] += __shfl_xor(s3[i], off, 64);
+      }
+    }
+    if (zl == 0) {
+      if constexpr (DUAL)
+        epi(m, n, s, s3);
+      else
+        epi(m, n, s);
+    }
   }
 }
 
 // ------------------------------------------------------------------ launch
+template <bool DUAL, class Epi>
+hipError_t launch_reduce(const float* partial, int splits, int M, int N, Epi epi, hipStream_t st) {
+  const int64_t groups = (int64_t)M * (N / 4);
+  if (groups < 32768) {
+    const int blocks = (int)((groups * 8 + kThreads - 1) / kThreads);
+    splitk_reduce<DUAL, 8, Epi><<<blocks, kThreads, 0, st>>>(partial, splits, M, N, epi);
+  } else {
+    const int blocks = (int)((groups + kThreads - 1) / kThreads);
+    splitk_reduce<DUAL, 1, Epi><<<blocks < 16384 ? blocks : 16384, kThreads, 0, st>>>(partial, splits, M, N, epi);
+  }
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int WAVES_M, int NS, bool DUAL, class Epi>
+hipError_t launch_dma(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, int N, int K, Epi epi, int splits,
+                      float* partial, hipStream_t st) {
+  const int bn_out = DUAL ? BN / 2 : BN;
+  const int tiles = ((M + BM - 1) / BM) * ((N + bn_out - 1) / bn_out);
+  int kps = (K + splits - 1) / splits;
+  kps = (kps + BK - 1) / BK * BK;
+  dim3 grid(tiles, 1, splits);
+  if (splits > 1)
+    gemm_bf16_dma<BM, BN, BK, WAVES_M, NS, DUAL, true, Epi>
+        <<<grid, kThreads, 0, st>>>(A, lda, w, M, N, K, kps, epi, partial);
+  else
+    gemm_bf16_dma<BM, BN, BK, WAVES_M, NS, DUAL, false, Epi>
+        <<<grid, kThreads, 0, st>>>(A, lda, w, M, N, K, kps, epi, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits <= 1) return e;
+  return launch_reduce<DUAL, Epi>(partial, splits, M, N, epi, st);
+}
 template <int BM, int BN, int WM_, int WN_, bool DUAL, class Epi>
 hipError_t launch_mfma(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, int N, int K, Epi epi,
                        int splits, float* partial, hipStream_t st) {
@@ -510,6 +587,11 @@ hipError_t launch_mfma(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, in
 template <bool DUAL, class Epi>
 hipError_t launch_bf16(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, int N, int K, Epi epi,
                        int splits, float* partial, hipStream_t st) {
+  // the DMA-pipelined kernels need K (and each split's K range) in whole 32-wide tiles
+  const bool dma = K % 32 == 0 && lda % 8 == 0;
+  if (dma && M <= 64) return launch_dma<64, 256, kSkinnyBK, 1, kSkinnyStages, DUAL>(A, lda, w, M, N, K, epi, splits,
+                                                                                   partial, st);
+  if (dma && splits <= 1) return launch_dma<256, 256, 32, 2, kStages, DUAL>(A, lda, w, M, N, K, epi, 1, partial, st);
   hipError_t e;
   if (M <= 32) {
     if constexpr (DUAL)
@@ -519,18 +601,10 @@ hipError_t launch_bf16(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, in
   } else if (M <= 64) {
     e = launch_mfma<64, 256, 2, 2, DUAL>(A, lda, w, M, N, K, epi, splits, partial, st);
   } else {
-    if (splits <= 1 && K % 32 == 0 && lda % 8 == 0 && K / 32 >= 1) {
-      const int bn_out = DUAL ? 128 : 256;
-      const int tiles = ((M + 255) / 256) * ((N + bn_out - 1) / bn_out);
-      gemm_bf16_dma<kStages, DUAL, Epi><<<tiles, kThreads, 0, st>>>(A, lda, w, M, N, K, epi);
-      return hipGetLastError();
-    }
     e = launch_mfma<256, 256, 2, 2, DUAL>(A, lda, w, M, N, K, epi, splits, partial, st);
   }
   if (e != hipSuccess || splits <= 1) return e;
-  int groups = (int)(((int64_t)M * (N / 4) + kThreads - 1) / kThreads);
-  splitk_reduce<DUAL, Epi><<<min(groups, 4096), kThreads, 0, st>>>(partial, splits, M, N, epi);
-  return hipGetLastError();
+  return launch_reduce<DUAL, Epi>(partial, splits, M, N, epi, st);
 }
 
 template <bool DUAL, class Epi>
@@ -546,24 +620,33 @@ hipError_t launch_f32(const float* A, int64_t lda, WeightRows<float> w, int M, i
     gemm_f32_fma<DUAL, false, Epi><<<grid, kThreads, 0, st>>>(A, lda, w, M, N, K, kps, epi, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits <= 1) return e;
-  int groups = (int)(((int64_t)M * (N / 4) + kThreads - 1) / kThreads);
-  splitk_reduce<DUAL, Epi><<<min(groups, 4096), kThreads, 0, st>>>(partial, splits, M, N, epi);
-  return hipGetLastError();
+  return launch_reduce<DUAL, Epi>(partial, splits, M, N, epi, st);
 }
 
 }  // namespace
 
 int gemm_pick_splits(int M, int N, int K, bool dual, bool is_bf16) {
   if (M > 64) return 1;
-  // small token count: the weights stream from HBM; split K until there are
-  // enough workgroups in flight to cover all 256 CUs several times over
-  int bn = is_bf16 ? (dual ? 128 : (M <= 32 ? 128 : 256)) : 64;
-  if (is_bf16 && M > 32) bn = dual ? 128 : 256;
-  int tiles = (N + bn - 1) / bn;
-  int bk = is_bf16 ? 64 : 16;
-  int max_splits = K / (bk * 4);  // keep >= 4 k-tiles per split
+  // small token count: the weights stream from HBM; split K until the grid
+  // covers the 256 CUs at the kernel's occupancy, keeping >= 4 k-tiles per split
+  int bn, bk, target;
+  if (is_bf16 && K % 32 == 0) {          // LDS-DMA kernel, 64 x 256 tiles
+    bn = dual ? 128 : 256;
+    bk = kSkinnyBK;
+    target = 512;
+  } else if (is_bf16) {                  // register-staged kernel
+    bn = (dual || M <= 32) ? 128 : 256;
+    bk = 64;
+    target = 1024;
+  } else {
+    bn = 64;
+    bk = 16;
+    target = 1024;
+  }
+  const int tiles = (N + bn - 1) / bn;
+  const int max_splits = K / (bk * 4);
   int s = 1;
-  while (tiles * s < 1024 && s * 2 <= max_splits && s < 32) s *= 2;
+  while (tiles * s < target && s * 2 <= max_splits && s < 32) s *= 2;
   return s;
 }
 
