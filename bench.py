@@ -92,7 +92,14 @@ def time_prefill(r, x, steps, warmup, p0=0):
 
 
 def flush_mall(buf):
-    buf.add_(1)  # 512 MiB write evicts the 256 MB Infinity Cache between decode reps
+    """Evicts the 256 MB Infinity Cache (and L2) between decode reps by READING 1 GiB.
+
+    A write-based flush leaves dirty lines whose write-back then competes with
+    the timed step's weight stream (measured: a cold 896 MiB read drops from
+    6.2 to 4.5 TB/s after a 512 MiB memset), which is not what a decode step
+    sees after the previous layer's (read-only) weight stream.
+    """
+    buf.sum()
 
 
 def time_decode(r, xs, p0s, flush):
@@ -250,7 +257,7 @@ def main():
     torch.cuda.empty_cache()
 
     if not a.prefill_only:
-        flush = torch.zeros(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+        flush = torch.zeros(1024 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
         # ------------------------------------------------------------ 8B-shaped prefill 8192 + decode
         log("workload llama3-8b-block: prefill 8192 then decode steps")
         w3, wts3, r3 = make_runner(3, dev)

@@ -20,8 +20,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kStages = 4;        // LDS ring depth of the DMA-pipelined kernel, large M (BK = 32)
+constexpr int kCUs = 256;         // MI355X compute units
 constexpr int kSkinnyBK = 64;     // small M: 128-byte row pieces per k-tile
-constexpr int kSkinnyStages = 3;  // small M: ring depth (3 x 40 KiB)
+constexpr int kSkinnyStages = 4;  // small M: ring depth (4 x 40 KiB fills the LDS)
 
 template <typename T>
 __device__ __forceinline__ const T* weight_row(const WeightRows<T>& w, int n, int K) {
@@ -555,6 +556,8 @@ hipError_t launch_dma(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, int
   const int tiles = ((M + BM - 1) / BM) * ((N + bn_out - 1) / bn_out);
   int kps = (K + splits - 1) / splits;
   kps = (kps + BK - 1) / BK * BK;
+  // every split must own at least one whole k-tile
+  if (K % BK != 0 || K < BK || (int64_t)(splits - 1) * kps >= K) return hipErrorInvalidValue;
   dim3 grid(tiles, 1, splits);
   if (splits > 1)
     gemm_bf16_dma<BM, BN, BK, WAVES_M, NS, DUAL, true, Epi>
@@ -587,11 +590,12 @@ hipError_t launch_mfma(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, in
 template <bool DUAL, class Epi>
 hipError_t launch_bf16(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, int N, int K, Epi epi,
                        int splits, float* partial, hipStream_t st) {
-  // the DMA-pipelined kernels need K (and each split's K range) in whole 32-wide tiles
-  const bool dma = K % 32 == 0 && lda % 8 == 0;
-  if (dma && M <= 64) return launch_dma<64, 256, kSkinnyBK, 1, kSkinnyStages, DUAL>(A, lda, w, M, N, K, epi, splits,
-                                                                                   partial, st);
-  if (dma && splits <= 1) return launch_dma<256, 256, 32, 2, kStages, DUAL>(A, lda, w, M, N, K, epi, 1, partial, st);
+  // the DMA-pipelined kernels need K (and each split's K range) in whole k-tiles
+  // (BK = kSkinnyBK for small M, 32 otherwise) and 16-byte aligned rows
+  if (lda % 8 == 0 && M <= 64 && K % kSkinnyBK == 0)
+    return launch_dma<64, 256, kSkinnyBK, 1, kSkinnyStages, DUAL>(A, lda, w, M, N, K, epi, splits, partial, st);
+  if (lda % 8 == 0 && M > 64 && K % 32 == 0 && splits <= 1)
+    return launch_dma<256, 256, 32, 2, kStages, DUAL>(A, lda, w, M, N, K, epi, 1, partial, st);
   hipError_t e;
   if (M <= 32) {
     if constexpr (DUAL)
@@ -627,26 +631,32 @@ hipError_t launch_f32(const float* A, int64_t lda, WeightRows<float> w, int M, i
 
 int gemm_pick_splits(int M, int N, int K, bool dual, bool is_bf16) {
   if (M > 64) return 1;
-  // small token count: the weights stream from HBM; split K until the grid
-  // covers the 256 CUs at the kernel's occupancy, keeping >= 4 k-tiles per split
-  int bn, bk, target;
-  if (is_bf16 && K % 32 == 0) {          // LDS-DMA kernel, 64 x 256 tiles
-    bn = dual ? 128 : 256;
-    bk = kSkinnyBK;
-    target = 512;
-  } else if (is_bf16) {                  // register-staged kernel
+  // small token count: the weights stream from HBM once; split K so that the
+  // grid covers the CUs
+  if (is_bf16 && K % kSkinnyBK == 0) {
+    // LDS-DMA kernel: its ring fills a CU's LDS, so one workgroup per CU; aim at
+    // one wave of workgroups (fewer splits measured faster than oversubscribing:
+    // every split adds an fp32 partial tile and shortens the pipeline)
+    const int tiles = (N + (dual ? 127 : 255)) / (dual ? 128 : 256);
+    const int nkt = K / kSkinnyBK;
+    int s = tiles >= kCUs ? 1 : kCUs / tiles;
+    s = min(s, max(1, nkt / kSkinnyStages));
+    // every split must own at least one k-tile: use the count the rounding yields
+    const int per = (nkt + s - 1) / s;
+    return (nkt + per - 1) / per;
+  }
+  int bn, bk;
+  if (is_bf16) {                         // register-staged kernel
     bn = (dual || M <= 32) ? 128 : 256;
     bk = 64;
-    target = 1024;
   } else {
     bn = 64;
     bk = 16;
-    target = 1024;
   }
   const int tiles = (N + bn - 1) / bn;
   const int max_splits = K / (bk * 4);
   int s = 1;
-  while (tiles * s < target && s * 2 <= max_splits && s < 32) s *= 2;
+  while (tiles * s < 1024 && s * 2 <= max_splits && s < 32) s *= 2;
   return s;
 }
 

@@ -84,6 +84,9 @@ def test_rope_apply(dtype):
 # ----------------------------------------------------------------------------- GEMM
 @pytest.mark.parametrize("dtype,M,K,N", [
     ("bf16", 5, 256, 100),        # skinny path, ragged N
+    ("bf16", 3, 32, 72),          # small M, K below one 64-wide k-tile
+    ("bf16", 17, 96, 300),        # small M, K = 64 + 32 (not whole 64-wide k-tiles)
+    ("bf16", 33, 4096, 640),      # small M, LDS-DMA kernel over 64 k-tiles
     ("bf16", 50, 520, 388),       # 64-row path, K tail (520 = 8*64 + 8)
     ("bf16", 300, 1024, 1000),    # large tiles with ragged M and N (LDS-DMA pipeline)
     ("bf16", 200, 1000, 260),     # large tiles, K not a multiple of 32 (register-staged kernel)
@@ -103,7 +106,11 @@ def test_linear(dtype, M, K, N):
 
 
 @pytest.mark.parametrize("dtype,rows,dim,hidden", [
-    ("bf16", 300, 256, 768), ("bf16", 20, 512, 1536), ("bf16", 64, 256, 776), ("f32", 40, 256, 768)])
+    ("bf16", 300, 256, 768), ("bf16", 20, 512, 1536), ("bf16", 64, 256, 776), ("f32", 40, 256, 768),
+    # small M with split K: w1/w3 in 4 splits; w2 (K = 2816 = 44 k-tiles) in 11 splits of 4
+    ("bf16", 9, 1024, 2816),
+    # small M, dim = 352 is not whole 64-wide k-tiles (register-staged kernel for w1/w3)
+    ("bf16", 7, 352, 1024)])
 def test_swiglu_ffn(dtype, rows, dim, hidden):
     need_gpu()
     print(f"case swiglu {dtype} rows={rows} dim={dim} hidden={hidden}", flush=True)
