@@ -39,6 +39,8 @@ int model_dims(const llama_model_args* a, llama_dtype dt, Dims* o) {
   if (a->dim % H != 0 || H % Hkv != 0) return LLAMA_ERR_INVALID_ARG;
   const int d = a->dim / H;
   if (d % 2 != 0) return LLAMA_ERR_INVALID_ARG;
+  // one sequence's cache rows are addressed with 32-bit element offsets
+  if ((int64_t)a->max_seq_len * Hkv * d > INT32_MAX) return LLAMA_ERR_UNSUPPORTED;
   int32_t F = 0;
   int rc = llama_ffn_hidden_dim(a, &F);
   if (rc != LLAMA_OK) return rc;

@@ -281,7 +281,7 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
 
 // ------------------------------------------------------------------ decode (bf16 MFMA, split-K)
 template <int HD>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const bf16* __restrict__ cv,
                  bf16* __restrict__ out, float* __restrict__ partial, AttnShape sh, int nsplit, int L,
                  float scale_log2) {
@@ -293,8 +293,10 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
   const int H = sh.n_heads, Hkv = sh.n_kv_heads;
   const int n_rep = H / Hkv;
   const int hgs = (n_rep + 15) / 16;
-  const int z = blockIdx.x;
-  const int j = blockIdx.y / hgs, hg = blockIdx.y % hgs;
+  // grid x walks the kv heads fastest: the workgroups that share each cache
+  // row (one 2*head_dim-byte piece per kv head) are dispatched together
+  const int j = blockIdx.x / hgs, hg = blockIdx.x % hgs;
+  const int z = blockIdx.y;
   const int b = blockIdx.z;
   const int T = sh.start_pos + 1;
   const int t_begin = z * L, t_end = min(T, t_begin + L);
@@ -323,21 +325,31 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
   const bool vtask = lane < 4 * CH;
   const int vg = lane / CH, vdc = lane % CH;
 
-  for (int c0 = t_begin + wave * 32; c0 < t_end; c0 += 128) {
-    bf16x8 kf[2][HD / 32];
+  // Each wave walks 32-key chunks c0, c0 + 128, ... of [t_begin, t_end).  The
+  // next chunk's K and V loads are issued before the current chunk is used, so
+  // the wave always has one chunk in flight.  Key indices are clamped to
+  // t_end - 1 (a row of this split that is always written): the loads need no
+  // guard and the softmax masks those keys out, so their V rows get weight 0.
+  // Offsets within one sequence's cache rows fit 32 bits (the host rejects
+  // max_seq * n_kv_heads * head_dim >= 2^31).
+  const int rstride = (int)stride;
+  auto load = [&](int c0, bf16x8 (&kf)[2][HD / 32], bf16x8 (&vk)[8]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const int key = c0 + kt * 16 + l16;
+      const int key = min(c0 + kt * 16 + l16, t_end - 1);
 #pragma unroll
       for (int kk = 0; kk < HD / 32; ++kk)
-        kf[kt][kk] = key < t_end ? *(const bf16x8*)(kbase + key * stride + (kk * 4 + g) * 8) : bf16x8{};
+        kf[kt][kk] = *(const bf16x8*)(kbase + (uint32_t)(key * rstride + (kk * 4 + g) * 8));
     }
-    bf16x8 vk[8];
+    if (vtask) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int key = c0 + (e < 4 ? vg * 4 + e : 16 + vg * 4 + (e - 4));
-      vk[e] = (vtask && key < t_end) ? *(const bf16x8*)(vbase + key * stride + vdc * 8) : bf16x8{};
+      for (int e = 0; e < 8; ++e) {
+        const int key = min(c0 + (e < 4 ? vg * 4 + e : 16 + vg * 4 + (e - 4)), t_end - 1);
+        vk[e] = *(const bf16x8*)(vbase + (uint32_t)(key * rstride + vdc * 8));
+      }
     }
+  };
+  auto compute = [&](int c0, const bf16x8 (&kf)[2][HD / 32], const bf16x8 (&vk)[8]) {
     if (vtask) {
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
@@ -393,7 +405,26 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  const int c_first = t_begin + wave * 32;
+  const int nit = c_first < t_end ? (t_end - c_first + 127) / 128 : 0;
+  bf16x8 kA[2][HD / 32], vA[8], kB[2][HD / 32], vB[8];
+  if (nit > 0) load(c_first, kA, vA);
+  int it = 0;
+  // (the scheduling barriers keep each prefetch ahead of the compute that
+  // would otherwise be hoisted above it and wait for every load in flight)
+  for (; it + 1 < nit; it += 2) {
+    load(c_first + (it + 1) * 128, kB, vB);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(c_first + it * 128, kA, vA);
+    __builtin_amdgcn_sched_barrier(0);
+    load(c_first + (it + 2) * 128, kA, vA);   // past the end: clamped rows, never used
+    __builtin_amdgcn_sched_barrier(0);
+    compute(c_first + (it + 1) * 128, kB, vB);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  if (it < nit) compute(c_first + it * 128, kA, vA);
 
   // merge the four waves' (max, sum, o) in LDS
   __syncthreads();
@@ -554,7 +585,7 @@ hipError_t attn_decode(const T* q, const T* cache_k, const T* cache_v, T* out, c
     int L = (T_ + ns - 1) / ns;
     L = (L + 31) / 32 * 32;
     const int n_rep = sh.n_heads / sh.n_kv_heads;
-    dim3 grid(ns, sh.n_kv_heads * ((n_rep + 15) / 16), sh.bsz);
+    dim3 grid(sh.n_kv_heads * ((n_rep + 15) / 16), ns, sh.bsz);
     if (sh.head_dim == 128)
       attn_decode_mfma<128><<<grid, 256, 0, st>>>(q, cache_k, cache_v, out, partial, sh, ns, L, scale * kLog2e);
     else

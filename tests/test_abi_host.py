@@ -108,6 +108,11 @@ def test_block_forward_validation_errors():
     assert _raw_block_forward(dba.ModelArgs(dim=256, n_heads=8, max_batch_size=2, max_seq_len=16)) == U  # d=32 bf16
     assert _raw_block_forward(dba.ModelArgs(dim=256, n_heads=8, max_batch_size=2, max_seq_len=16),
                               dtype=dba.LLAMA_F32) == W                             # d=32 is built for f32
+    # one sequence's cache rows (max_seq_len * n_kv_heads * head_dim) must stay below 2^31 elements
+    assert _raw_block_forward(dba.ModelArgs(dim=8192, n_heads=64, n_kv_heads=64, max_batch_size=1,
+                                            max_seq_len=1 << 18)) == U
+    assert _raw_block_forward(dba.ModelArgs(dim=8192, n_heads=64, n_kv_heads=8, max_batch_size=1,
+                                            max_seq_len=1 << 18)) == W
 
 
 def test_device_entry_points_reject_bad_arguments():

@@ -119,10 +119,14 @@ def test_swiglu_ffn(dtype, rows, dim, hidden):
     w2 = rnd((dim, hidden), 0.05, dtype)
     y = torch.empty(rows, dim, dtype=tdt(dtype), device="cuda:0")
     nbytes = dba.llama_ffn_workspace_size(rows, dim, hidden, dba.LLAMA_BF16 if dtype == "bf16" else dba.LLAMA_F32)
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda:0")
-    dba.llama_swiglu_ffn(dev(x), dev(w1), dev(w3), dev(w2), y, rows, dim, hidden, ws, nbytes)
-    torch.cuda.synchronize()
-    check(y, ob.swiglu_ffn(f64(x), f64(w1), f64(w3), f64(w2)), dtype, "swiglu")
+    ws = torch.full((max(nbytes, 1),), 0xA5, dtype=torch.uint8, device="cuda:0")   # junk on entry
+    ref = ob.swiglu_ffn(f64(x), f64(w1), f64(w3), f64(w2))
+    # twice on one workspace: the split reductions must leave their counters reusable
+    for rep in range(2):
+        y.fill_(float("nan"))
+        dba.llama_swiglu_ffn(dev(x), dev(w1), dev(w3), dev(w2), y, rows, dim, hidden, ws, nbytes)
+        torch.cuda.synchronize()
+        check(y, ref, dtype, f"swiglu call {rep}")
 
 
 # ----------------------------------------------------------------------------- attention
@@ -190,7 +194,8 @@ def test_attn_decode(dtype, B, p0, H, Hkv, d):
     gck, gcv = dev(ck), dev(cv)
     out = torch.empty(B, 1, H * d, dtype=tdt(dtype), device="cuda:0")
     nbytes = dba.llama_attn_decode_workspace_size(args, B, p0)
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda:0")
+    # a workspace full of junk: the call must clear its split counters itself
+    ws = torch.full((max(nbytes, 1),), 0xA5, dtype=torch.uint8, device="cuda:0")
     dba.llama_gqa_attn_decode(dev(q), dev(k), dev(v), gck, gcv, out, args, B, p0, ws, nbytes)
     torch.cuda.synchronize()
     rck, rcv = f64(ck), f64(cv)
