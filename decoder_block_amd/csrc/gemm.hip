@@ -19,7 +19,11 @@ namespace llama {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kStages = 4;        // LDS ring depth of the DMA-pipelined kernel, large M (BK = 32)
+// large M: 256 x 256 tiles, 64-deep k-tiles in a 2-stage LDS ring (2 x 64 KiB), eight
+// waves (two per SIMD: one wave's MFMAs cover the other's waits)
+constexpr int kBigBK = 64;
+constexpr int kBigStages = 2;
+constexpr int kBigWaves = 8;
 constexpr int kCUs = 256;         // MI355X compute units
 constexpr int kSkinnyBK = 64;     // small M: 128-byte row pieces per k-tile
 constexpr int kSkinnyStages = 4;  // small M: ring depth (4 x 40 KiB fills the LDS)
@@ -238,24 +242,24 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(63 | (7 << 4) | (0 << 8) | (3 << 14)); }
 
-template <int BM, int BN, int BK, int WAVES_M, int NS, bool DUAL, bool SPLIT, class Epi>
-__global__ void __launch_bounds__(kThreads)
+template <int BM, int BN, int BK, int WAVES_M, int NS, bool DUAL, bool SPLIT, class Epi, int NW>
+__global__ void __launch_bounds__(NW * 64)
 gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M, int N, int K, int k_per_split,
               Epi epi, float* __restrict__ partial) {
   constexpr int CH = BK / 8;                  // 16-byte chunks per tile row
   constexpr int RPB = 64 / CH;                // tile rows per 1 KiB DMA block
-  constexpr int WAVES_N = 4 / WAVES_M;
+  constexpr int WAVES_N = NW / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int ROWS = BM + BN;               // rows x 2*BK bytes per stage
   constexpr int BLOCKS = ROWS / RPB;          // 1 KiB DMA blocks per stage
-  constexpr int LOADS = BLOCKS / 4;           // per wave (and per lane) per stage
+  constexpr int LOADS = BLOCKS / NW;          // per wave (and per lane) per stage
   constexpr int BN_OUT = DUAL ? BN / 2 : BN;
   constexpr int RD = TN + TM;                 // fragment reads per 16-deep half
   constexpr int MF = TN * TM;                 // MFMAs per half
   static_assert(BK == 32 || BK == 64, "BK");
-  static_assert(NS >= 2 && BLOCKS % 4 == 0 && TM >= 1 && TN >= 1 && (!DUAL || TN % 2 == 0), "shape");
-  static_assert(MF % RD == 0, "interleave");
+  static_assert(NS >= 2 && BLOCKS % NW == 0 && TM >= 1 && TN >= 1 && (!DUAL || TN % 2 == 0), "shape");
+  static_assert(MF >= RD && WAVES_M * WAVES_N == NW, "interleave");
   __shared__ bf16x8 smem[NS][ROWS * CH];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -334,13 +338,15 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
       for (int b = 0; b < TM; ++b)
         acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
   };
-  // RD fragment reads spread over MF MFMAs
+  // the RD fragment reads for the next step go out one after each of the first
+  // RD MFMAs, leaving the last MF - RD MFMAs to cover their latency
   auto interleave = [&]() {
 #pragma unroll
     for (int i = 0; i < RD; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, MF / RD, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    if constexpr (MF > RD) __builtin_amdgcn_sched_group_barrier(0x008, MF - RD, 0);
   };
 
   constexpr int KS = BK / 16;                 // 16-deep MFMA steps per k-tile
@@ -549,7 +555,7 @@ hipError_t launch_reduce(const float* partial, int splits, int M, int N, Epi epi
   return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int WAVES_M, int NS, bool DUAL, class Epi>
+template <int BM, int BN, int BK, int WAVES_M, int NS, bool DUAL, int NW, class Epi>
 hipError_t launch_dma(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, int N, int K, Epi epi, int splits,
                       float* partial, hipStream_t st) {
   const int bn_out = DUAL ? BN / 2 : BN;
@@ -560,11 +566,11 @@ hipError_t launch_dma(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, int
   if (K % BK != 0 || K < BK || (int64_t)(splits - 1) * kps >= K) return hipErrorInvalidValue;
   dim3 grid(tiles, 1, splits);
   if (splits > 1)
-    gemm_bf16_dma<BM, BN, BK, WAVES_M, NS, DUAL, true, Epi>
-        <<<grid, kThreads, 0, st>>>(A, lda, w, M, N, K, kps, epi, partial);
+    gemm_bf16_dma<BM, BN, BK, WAVES_M, NS, DUAL, true, Epi, NW>
+        <<<grid, NW * 64, 0, st>>>(A, lda, w, M, N, K, kps, epi, partial);
   else
-    gemm_bf16_dma<BM, BN, BK, WAVES_M, NS, DUAL, false, Epi>
-        <<<grid, kThreads, 0, st>>>(A, lda, w, M, N, K, kps, epi, partial);
+    gemm_bf16_dma<BM, BN, BK, WAVES_M, NS, DUAL, false, Epi, NW>
+        <<<grid, NW * 64, 0, st>>>(A, lda, w, M, N, K, kps, epi, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits <= 1) return e;
   return launch_reduce<DUAL, Epi>(partial, splits, M, N, epi, st);
@@ -591,11 +597,11 @@ template <bool DUAL, class Epi>
 hipError_t launch_bf16(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, int N, int K, Epi epi,
                        int splits, float* partial, hipStream_t st) {
   // the DMA-pipelined kernels need K (and each split's K range) in whole k-tiles
-  // (BK = kSkinnyBK for small M, 32 otherwise) and 16-byte aligned rows
+  // (BK = kSkinnyBK for small M, kBigBK otherwise) and 16-byte aligned rows
   if (lda % 8 == 0 && M <= 64 && K % kSkinnyBK == 0)
-    return launch_dma<64, 256, kSkinnyBK, 1, kSkinnyStages, DUAL>(A, lda, w, M, N, K, epi, splits, partial, st);
-  if (lda % 8 == 0 && M > 64 && K % 32 == 0 && splits <= 1)
-    return launch_dma<256, 256, 32, 2, kStages, DUAL>(A, lda, w, M, N, K, epi, 1, partial, st);
+    return launch_dma<64, 256, kSkinnyBK, 1, kSkinnyStages, DUAL, 4>(A, lda, w, M, N, K, epi, splits, partial, st);
+  if (lda % 8 == 0 && M > 64 && K % kBigBK == 0 && splits <= 1)
+    return launch_dma<256, 256, kBigBK, 2, kBigStages, DUAL, kBigWaves>(A, lda, w, M, N, K, epi, 1, partial, st);
   hipError_t e;
   if (M <= 32) {
     if constexpr (DUAL)
