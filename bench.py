@@ -245,7 +245,7 @@ def main():
     dom = "w1w3_swiglu"
     dom_ms = stage_ms[STAGES.index(dom)]
     dom_ach = work[dom][1] / (dom_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": "gemm_bf16_mfma<DUAL> (w1/w3 + SwiGLU epilogue)",
+    roofline = {"bound": "mfma", "kernel": "gemm_bf16_dma<256x256x64, 8 waves, DUAL, EpiSwiGLU> (w1/w3 + SwiGLU)",
                 "achieved": round(dom_ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(dom_ach / PEAK_BF16_TFLOPS, 4), "traffic": kernel_traffic("w1w3_swiglu_llama7b"),
                 "kernel_ms": round(dom_ms, 4)}

@@ -38,7 +38,7 @@ __device__ __forceinline__ const T* weight_row(const WeightRows<T>& w, int n, in
 // Tile coordinates of a logical workgroup id: XCD-aware remap, then grouped
 // ordering (GROUP_M tile rows share their weight tiles in L2).
 __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int GROUP_M = 8;
+  constexpr int GROUP_M = 4;
   int nb = tiles_m * tiles_n;
   int pid = xcd_remap(blockIdx.x, nb);
   int in_group = GROUP_M * tiles_n;
