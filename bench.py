@@ -91,6 +91,27 @@ def time_prefill(r, x, steps, warmup, p0=0):
     return wall, stage_ms
 
 
+def time_chunked_prefill(r, x, chunk, steps, warmup):
+    """One prompt fed as consecutive chunks (start_pos 0, chunk, 2*chunk, ...): wall time per whole prompt."""
+    import torch
+    bsz, S, _ = x.shape
+    r.reserve(bsz, chunk, S - chunk)
+    parts = [x[:, c:c + chunk].contiguous() for c in range(0, S, chunk)]
+    outs = [torch.empty_like(p) for p in parts]
+
+    def once():
+        for i, (p, o) in enumerate(zip(parts, outs)):
+            r.forward(p, i * chunk, o)
+    for _ in range(warmup):
+        once()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        once()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
 def flush_mall(buf):
     """Evicts the 256 MB Infinity Cache (and L2) between decode reps by READING 1 GiB.
 
@@ -273,6 +294,10 @@ def main():
                 "gemm_mfma_frac": round(sum(work3[n][1] for n in ("qkv_rope_append", "wo_residual", "w1w3_swiglu",
                                                                    "w2_residual")) /
                                         (sum(stage3[i] for i in (1, 3, 5, 6)) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        # the same 8192-token prompt fed in 4 chunks of 2048 (each chunk attends to the cached prefix)
+        wallc = time_chunked_prefill(r3, xp, 2048, max(3, a.steps // 4), 1)
+        pre3["chunked_4x2048_tokens_per_s"] = round(S3 / wallc, 1)
+        pre3["chunked_4x2048_ms"] = round(wallc * 1e3, 3)
         nd = min(a.decode_steps, w3.decode_steps)
         xs = [x3[:, S3 + t:S3 + t + 1].contiguous() for t in range(nd)]
         tot, st = time_decode(r3, xs, [S3 + t for t in range(nd)], flush)

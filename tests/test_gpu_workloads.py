@@ -73,7 +73,7 @@ def test_llama7b_block_prefill_full_size():
     check(run.cache_v, cv, "bf16", "7B cache_v")
 
 
-def test_llama3_8b_block_prefill_then_128_decodes():
+def test_llama3_8b_block_prefill_chunked_prefill_and_128_decodes():
     dev = need_gpu()
     w = wl.WORKLOADS[3]
     print(f"case {w.name}: prefill {w.prefill_len} + {w.decode_steps} decodes bf16", flush=True)
@@ -84,9 +84,14 @@ def test_llama3_8b_block_prefill_then_128_decodes():
     gx = x.to(dev)
     pre = run.forward(gx[:, :S].contiguous(), 0)
     dec = [run.forward(gx[:, S + t:S + t + 1].contiguous(), S + t) for t in range(w.decode_steps)]
+    # the same prompt fed as 4 chunks of 2048 tokens (start_pos 0, 2048, 4096, 6144)
+    runc = BlockRunner(model_args_for(w), wts, torch.bfloat16, dev)
+    C = 2048
+    chunked = torch.cat([runc.forward(gx[:, c:c + C].contiguous(), c) for c in range(0, S, C)], dim=1)
     torch.cuda.synchronize()
     got = torch.cat([pre] + dec, dim=1)
-    rows = _rows(S, (4095, 4096)) + [S + t for t in (0, 1, 2, 31, 63, 64, 126, 127)]
+    prompt_rows = _rows(S, (2047, 2048, 4095, 4096, 6143, 6144))
+    rows = prompt_rows + [S + t for t in (0, 1, 2, 31, 63, 64, 126, 127)]
     shape = (w.batch, w.max_seq_len, w.n_kv_heads, w.head_dim)
     ck, cv = np.zeros(shape), np.zeros(shape)
     ref = ob.block_forward(f64(x), _w64(wts), ck, cv, 0, w.n_heads, w.n_kv_heads, w.norm_eps, w.rope_theta,
@@ -94,6 +99,9 @@ def test_llama3_8b_block_prefill_then_128_decodes():
     check(got[:, rows], ref, "bf16", "8B block sampled prefill + decode rows")
     check(run.cache_k, ck, "bf16", "8B cache_k")
     check(run.cache_v, cv, "bf16", "8B cache_v")
+    check(chunked[:, prompt_rows], ref[:, :len(prompt_rows)], "bf16", "8B chunked prefill (4 x 2048) sampled rows")
+    check(runc.cache_k[:, :S], ck[:, :S], "bf16", "8B chunked prefill cache_k")
+    check(runc.cache_v[:, :S], cv[:, :S], "bf16", "8B chunked prefill cache_v")
 
 
 def test_llama2_70b_block_decode_batch32():
