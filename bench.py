@@ -207,9 +207,23 @@ def bench_stack(dev, steps):
     pre = e[0].elapsed_time(e[1])
     dec = e[1].elapsed_time(e[2]) / steps
     log(f"stack prefill {pre:.1f} ms, decode {dec:.3f} ms/step")
+    # top-p sampling of the last step's logits (temperature 0.8, top_p 0.95: the walkthrough's defaults)
+    g = torch.Generator(device=dev).manual_seed(5)
+    uni = torch.rand(20, w.batch, generator=g, device=dev)
+    from decoder_block_amd import _lib as L
+    L.llama_sample_top_p(logits, out[0], w.batch, w.vocab_size, 0.8, 0.95, uni[0])
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for i in range(20):
+        L.llama_sample_top_p(logits, out[0], w.batch, w.vocab_size, 0.8, 0.95, uni[i])
+    s1.record()
+    torch.cuda.synchronize()
+    samp = s0.elapsed_time(s1) / 20
     res = {"prefill_ms": round(pre, 2), "prefill_tokens_per_s": round(w.batch * w.prefill_len / pre * 1e3, 1),
            "decode_ms_per_step": round(dec, 3), "decode_tokens_per_s": round(w.batch / dec * 1e3, 1),
-           "decode_steps_timed": steps, "batch": w.batch, "prompt": w.prefill_len, "layers": w.n_layers}
+           "decode_steps_timed": steps, "batch": w.batch, "prompt": w.prefill_len, "layers": w.n_layers,
+           "top_p_sampling_us": round(samp * 1e3, 1)}
     del stack
     torch.cuda.empty_cache()
     return res

@@ -29,7 +29,7 @@ EXPORTS = (
     "llama_attn_decode_workspace_size", "llama_ffn_workspace_size", "llama_rope_freqs",
     "llama_rmsnorm", "llama_rope", "llama_gqa_attn_prefill", "llama_gqa_attn_decode",
     "llama_swiglu_ffn", "llama_linear", "llama_block_forward", "llama_block_forward_events", "llama_embedding",
-    "llama_lm_head_workspace_size", "llama_lm_head_argmax",
+    "llama_lm_head_workspace_size", "llama_lm_head_argmax", "llama_sample_top_p",
 )
 
 
@@ -105,6 +105,7 @@ def lib() -> ctypes.CDLL:
                                             SZ, ctypes.c_int, P, ctypes.POINTER(P)], ctypes.c_int),
             "llama_embedding": ([P, P, P, I64, I32, I32, ctypes.c_int, P], ctypes.c_int),
             "llama_lm_head_argmax": ([P, I64, P, P, P, P, I32, I32, I32, F, P, SZ, ctypes.c_int, P], ctypes.c_int),
+            "llama_sample_top_p": ([P, P, I32, I32, F, F, P, P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -263,3 +264,10 @@ def llama_lm_head_argmax(h, h_row_stride: int, norm_w, w_out, logits, next_tok, 
     _check(lib().llama_lm_head_argmax(_ptr(h), h_row_stride, _ptr(norm_w), _ptr(w_out), _ptr(logits),
                                       _ptr(next_tok), bsz, dim, vocab, eps, _ptr(ws), ws_bytes, _dtype(h),
                                       _stream(stream)), "llama_lm_head_argmax")
+
+
+def llama_sample_top_p(logits, next_tok, bsz: int, vocab: int, temperature: float, top_p: float, uniforms=None,
+                       stream=None) -> None:
+    _check(lib().llama_sample_top_p(_ptr(logits), _ptr(next_tok), bsz, vocab, temperature, top_p,
+                                    _ptr(uniforms) if uniforms is not None else None, _stream(stream)),
+           "llama_sample_top_p")

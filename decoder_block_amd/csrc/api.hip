@@ -12,6 +12,7 @@
 #include "attention.hpp"
 #include "gemm.hpp"
 #include "misc.hpp"
+#include "sample.hpp"
 
 using llama::bf16;
 
@@ -492,6 +493,16 @@ int llama_lm_head_argmax(const void* h, int64_t h_row_stride, const void* norm_w
   }
   if (e == hipSuccess) e = llama::argmax_rows(logits, next, bsz, vocab, st);
   return hip_status(e);
+}
+
+int llama_sample_top_p(const float* logits, int32_t* next, int32_t bsz, int32_t vocab, float temperature,
+                       float top_p, const float* uniforms, llama_stream_t stream) {
+  if (!logits || !next || bsz < 1 || vocab < 1) return LLAMA_ERR_INVALID_ARG;
+  if (temperature != temperature || top_p != top_p) return LLAMA_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  if (!(temperature > 0.f)) return hip_status(llama::argmax_rows(logits, next, bsz, vocab, st));
+  if (!uniforms) return LLAMA_ERR_INVALID_ARG;
+  return hip_status(llama::sample_top_p(logits, next, bsz, vocab, temperature, top_p, uniforms, st));
 }
 
 }  // extern "C"

@@ -137,18 +137,35 @@ __global__ void embedding_kernel(const int32_t* __restrict__ tok, const T* __res
 }
 
 // Greedy token: argmax of a fp32 row, the lowest index among equal maxima.
-__global__ void __launch_bounds__(kThreads) argmax_kernel(const float* __restrict__ logits,
-                                                          int32_t* __restrict__ next, int cols) {
-  __shared__ float bv[kThreads / 64];
-  __shared__ int bi[kThreads / 64];
+// 1024 threads per row; VEC: 16-byte loads (vocab % 4 == 0, aligned rows).
+constexpr int kArgmaxThreads = 1024;
+template <bool VEC>
+__global__ void __launch_bounds__(kArgmaxThreads) argmax_kernel(const float* __restrict__ logits,
+                                                                int32_t* __restrict__ next, int cols) {
+  __shared__ float bv[kArgmaxThreads / 64];
+  __shared__ int bi[kArgmaxThreads / 64];
   const float* r = logits + (int64_t)blockIdx.x * cols;
   float best = -INFINITY;
   int idx = 0x7fffffff;
-  for (int c = threadIdx.x; c < cols; c += kThreads) {
-    float v = r[c];
-    if (v > best) {  // strided scan visits increasing c: keep the first maximum
-      best = v;
-      idx = c;
+  // each thread visits its columns in increasing order and keeps the first maximum
+  if constexpr (VEC) {
+    const f32x4* rv = (const f32x4*)r;
+    for (int v = threadIdx.x; v < cols / 4; v += kArgmaxThreads) {
+      const f32x4 x = rv[v];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (x[e] > best) {
+          best = x[e];
+          idx = 4 * v + e;
+        }
+    }
+  } else {
+    for (int c = threadIdx.x; c < cols; c += kArgmaxThreads) {
+      const float v = r[c];
+      if (v > best) {
+        best = v;
+        idx = c;
+      }
     }
   }
 #pragma unroll
@@ -166,7 +183,7 @@ __global__ void __launch_bounds__(kThreads) argmax_kernel(const float* __restric
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int i = 1; i < kThreads / 64; ++i)
+    for (int i = 1; i < kArgmaxThreads / 64; ++i)
       if (bv[i] > best || (bv[i] == best && bi[i] < idx)) {
         best = bv[i];
         idx = bi[i];
@@ -215,7 +232,10 @@ hipError_t embedding(const int32_t* tok, const T* table, T* out, int64_t n, int 
 
 hipError_t argmax_rows(const float* logits, int32_t* next, int rows, int cols, hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  argmax_kernel<<<rows, kThreads, 0, st>>>(logits, next, cols);
+  if (cols % 4 == 0 && (uintptr_t)logits % 16 == 0)
+    argmax_kernel<true><<<rows, kArgmaxThreads, 0, st>>>(logits, next, cols);
+  else
+    argmax_kernel<false><<<rows, kArgmaxThreads, 0, st>>>(logits, next, cols);
   return hipGetLastError();
 }
 

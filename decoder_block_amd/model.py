@@ -1,12 +1,13 @@
-"""Whole-model greedy generation on one GPU through the C ABI.
+"""Whole-model generation on one GPU through the C ABI.
 
 Token embedding -> n_layers x llama_block_forward -> final RMSNorm + output
-projection of the last position -> argmax, with the greedy token written on
-the device and fed straight back as the next call's input (no host round trip
-per token).  Follows the linkmax.top walkthrough of Meta's LLaMA code,
+projection of the last position -> argmax or top-p sampling, with the token
+written on the device and fed straight back as the next call's input (no host
+round trip per token).  Follows the linkmax.top walkthrough of Meta's LLaMA code,
 section 3.2.2 (Transformer.forward: embedding, layers, norm, output on the last
 position) and section 3.3 (generate: one prefill call, then one-token calls at
-the previous position; argmax when the temperature is 0).
+the previous position; argmax when the temperature is 0, else softmax at the
+temperature and sample_top_p).
 
 torch only allocates device memory and provides the stream; every step of the
 forward pass runs in the HIP library.
@@ -76,19 +77,29 @@ class StackRunner:
         L.llama_lm_head_argmax(last, seqlen * D, self.norm_w, self.w_out, logits, next_tok, bsz, D, self.vocab,
                                self.args.norm_eps, self.ws, ws_bytes)
 
-    def generate(self, prompt: torch.Tensor, steps: int, on_step=None) -> torch.Tensor:
-        """Greedy generation: prefill the prompt, then ``steps`` one-token calls.
-        Returns the generated ids [steps + 1, bsz]: row t is the device-side argmax
-        of call t and is passed, as is, as the input ids of call t + 1 (no host
-        synchronisation inside the loop)."""
+    def generate(self, prompt: torch.Tensor, steps: int, on_step=None, temperature: float = 0.0,
+                 top_p: float = 0.95, uniforms: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Generation: prefill the prompt, then ``steps`` one-token calls.
+        Returns the generated ids [steps + 1, bsz]: row t is chosen on the device
+        from call t's logits and is passed, as is, as the input ids of call t + 1
+        (no host synchronisation inside the loop).  temperature 0 takes the argmax;
+        a positive temperature samples with the nucleus cut top_p, call t drawing
+        with uniforms[t] ([steps + 1, bsz] floats in [0, 1), on the device)."""
         bsz, S = prompt.shape
         out = torch.empty(steps + 1, bsz, dtype=torch.int32, device=self.device)
         logits = torch.empty(bsz, self.vocab, dtype=torch.float32, device=self.device)
+        sampled = temperature > 0
+        if sampled and (uniforms is None or tuple(uniforms.shape) != (steps + 1, bsz)):
+            raise ValueError("sampling needs uniforms of shape [steps + 1, bsz] on the device")
+
+        def pick(t):
+            if sampled:
+                L.llama_sample_top_p(logits, out[t], bsz, self.vocab, temperature, top_p, uniforms[t])
+            if on_step is not None:
+                on_step(t, logits, out[t])
         self.forward(prompt, 0, logits, out[0])
-        if on_step is not None:
-            on_step(0, logits, out[0])
+        pick(0)
         for t in range(steps):
             self.forward(out[t].view(bsz, 1), S + t, logits, out[t + 1])
-            if on_step is not None:
-                on_step(t + 1, logits, out[t + 1])
+            pick(t + 1)
         return out

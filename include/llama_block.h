@@ -233,6 +233,21 @@ int llama_lm_head_argmax(const void* h, int64_t h_row_stride, const void* norm_w
                          int32_t dim, int32_t vocab, float eps, void* ws, size_t ws_bytes,
                          llama_dtype dtype, llama_stream_t stream);
 
+/* Next token per row by temperature + nucleus (top-p) sampling (linkmax.top walkthrough,
+ * section 3.3, generate and sample_top_p): probabilities softmax(logits / temperature);
+ * tokens in descending probability, equal probabilities by ascending id; a token is kept
+ * when the probability before it in that order is <= top_p (the first is always kept);
+ * the kept probabilities are renormalised and the token drawn is the first whose
+ * cumulative kept probability exceeds uniforms[b] (inverse-CDF draw: uniforms[b] in
+ * [0, 1) supplies the randomness, so the call is deterministic).  temperature <= 0 takes
+ * the argmax (lowest id among equal maxima) and ignores top_p and uniforms.
+ * logits: device float [bsz][vocab], finite; next: device int32 [bsz]; uniforms: device
+ * float [bsz] (may be NULL when temperature <= 0).  Requires top_p not NaN.  No workspace;
+ * the arithmetic is fp32 per token with fp64 sums, deterministic for given inputs. */
+int llama_sample_top_p(const float* logits, int32_t* next, int32_t bsz, int32_t vocab,
+                       float temperature, float top_p, const float* uniforms,
+                       llama_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -143,4 +143,10 @@ def test_device_entry_points_reject_bad_arguments():
     assert lib.llama_swiglu_ffn(p, p, p, p, p, 4, 256, 768, p, 0, dba.LLAMA_BF16, None) == \
         dba._lib.LLAMA_ERR_WORKSPACE_TOO_SMALL
     assert lib.llama_embedding(p, p, p, 4, 250, 10, dba.LLAMA_BF16, None) == E
+    assert lib.llama_sample_top_p(None, p, 4, 100, 0.8, 0.9, p, None) == E             # no logits
+    assert lib.llama_sample_top_p(p, p, 0, 100, 0.8, 0.9, p, None) == E                # bsz < 1
+    assert lib.llama_sample_top_p(p, p, 4, 0, 0.8, 0.9, p, None) == E                  # vocab < 1
+    assert lib.llama_sample_top_p(p, p, 4, 100, 0.8, float("nan"), p, None) == E       # top_p NaN
+    assert lib.llama_sample_top_p(p, p, 4, 100, float("nan"), 0.9, p, None) == E       # temperature NaN
+    assert lib.llama_sample_top_p(p, p, 4, 100, 0.8, 0.9, None, None) == E             # sampling needs uniforms
     assert lib.llama_lm_head_argmax(p, 100, p, p, p, p, 2, 256, 1000, 1e-5, p, 1 << 30, dba.LLAMA_BF16, None) == E

@@ -110,3 +110,29 @@ def test_stack_full_workload_greedy_generation(host_weights):
         assert np.all(np.isfinite(lg))
         np.testing.assert_array_equal(nxt, np.argmax(lg, axis=1))   # greedy = argmax, lowest id on ties
         np.testing.assert_array_equal(ids[t], nxt)                   # and that id was fed to the next call
+
+
+def test_stack_top_p_sampled_generation(host_weights):
+    """Sampled generation (temperature 0.8, top_p 0.95) through the whole stack: the
+    sampled ids are in range, are what the next call consumes, are reproducible for
+    the same uniform numbers, and depart from greedy.  The selection kernel itself is
+    checked against the oracle in test_gpu_sampling.py on seeded logits."""
+    dev = need_gpu()
+    layers, emb, norm_w, w_out = host_weights
+    w = W5
+    steps, S = 8, 128
+    print(f"case {w.name}: B={w.batch} prompt {S} + {steps} sampled steps (T=0.8, top_p=0.95)", flush=True)
+    stack = StackRunner(model_args_for(w), lambda l: layers[l], emb, norm_w, w_out, torch.bfloat16, dev)
+    prompt = wl.prompt_tokens(w)[:, :S].contiguous().to(dev)
+    g = torch.Generator(device=dev).manual_seed(99)
+    uni = torch.rand(steps + 1, w.batch, generator=g, device=dev)
+    a = stack.generate(prompt, steps, temperature=0.8, top_p=0.95, uniforms=uni).cpu().numpy()
+    b = stack.generate(prompt, steps, temperature=0.8, top_p=0.95, uniforms=uni).cpu().numpy()
+    greedy = stack.generate(prompt, steps).cpu().numpy()
+    torch.cuda.synchronize()
+    assert a.shape == (steps + 1, w.batch)
+    assert a.min() >= 0 and a.max() < w.vocab_size
+    np.testing.assert_array_equal(a, b)
+    assert np.mean(a[0] != greedy[0]) > 0.5        # flat synthetic logits: sampling rarely picks the argmax
+    del stack
+    torch.cuda.empty_cache()
