@@ -409,7 +409,7 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
             epi(m, n, v1, v3);
           }
         }
-    } else {
+    } else if constexpr (SPLIT) {
 #pragma unroll
       for (int a = 0; a < TN; ++a)
 #pragma unroll
@@ -417,10 +417,27 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
           const int n = n0 + wn * WN + a * 32 + g * 8 + lhalf * 4;
           if (n >= N) continue;
           f32x4 v = {acc[a][b][g * 4], acc[a][b][g * 4 + 1], acc[a][b][g * 4 + 2], acc[a][b][g * 4 + 3]};
-          if (SPLIT)
-            *(f32x4*)(partial + ((int64_t)blockIdx.z * M + m) * (int64_t)N + n) = v;
-          else
-            epi(m, n, v);
+          *(f32x4*)(partial + ((int64_t)blockIdx.z * M + m) * (int64_t)N + n) = v;
+        }
+    } else {
+      // row-dependent parts once, then the fragment's epilogue loads, then its stores
+      const auto row = epi_row(epi, m);
+      decltype(epi_pre(epi, row, 0)) pre[TN][4];
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * WN + a * 32 + g * 8 + lhalf * 4;
+          pre[a][g] = epi_pre(epi, row, min(n, N - 4));
+        }
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * WN + a * 32 + g * 8 + lhalf * 4;
+          if (n >= N) continue;
+          f32x4 v = {acc[a][b][g * 4], acc[a][b][g * 4 + 1], acc[a][b][g * 4 + 2], acc[a][b][g * 4 + 3]};
+          epi_apply(epi, row, n, v, pre[a][g]);
         }
     }
   }

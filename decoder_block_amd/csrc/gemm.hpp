@@ -53,7 +53,8 @@ struct EpiF32 {
 // QKV epilogue: columns [0, nq) are q, [nq, nq+nkv) are k, the rest v.  q and k
 // get the interleaved-pair rotation of their position (start_pos + m % seqlen)
 // from the fp32 (cos, sin) table; q goes to q_out [M][nq]; k and v are written
-// straight into the caches at [b][start_pos + s] (cache append).
+// straight into the caches at [b][start_pos + s] (cache append).  head_dim is a
+// power of two.
 template <typename T>
 struct EpiQKV {
   T* q_out;
@@ -62,27 +63,83 @@ struct EpiQKV {
   const float* freqs;  // [freqs_end][head_dim/2][2]
   int seqlen, start_pos, max_seq, nq, nkv, head_dim;
   const float* rscale; // optional per-row RMSNorm factor applied to the accumulators
-  __device__ __forceinline__ f32x4 rope(f32x4 v, int pos, int e) const {
-    const float* f = freqs + ((int64_t)pos * (head_dim >> 1) + (e >> 1)) * 2;
-    f32x4 cs = *(const f32x4*)f;  // cos_i, sin_i, cos_{i+1}, sin_{i+1}
+  // (cos_i, sin_i, cos_i+1, sin_i+1) of columns n..n+3 (zero for v columns)
+  __device__ __forceinline__ f32x4 cos_sin(int m, int n) const {
+    if (n >= nq + nkv) return f32x4{};
+    const int pos = start_pos + (m - (m / seqlen) * seqlen);
+    const int e = (n < nq ? n : n - nq) & (head_dim - 1);
+    return *(const f32x4*)(freqs + ((int64_t)pos * (head_dim >> 1) + (e >> 1)) * 2);
+  }
+  __device__ __forceinline__ static f32x4 rotate(f32x4 v, f32x4 cs) {
     return f32x4{v[0] * cs[0] - v[1] * cs[1], v[0] * cs[1] + v[1] * cs[0],
                  v[2] * cs[2] - v[3] * cs[3], v[2] * cs[3] + v[3] * cs[2]};
   }
-  __device__ __forceinline__ void operator()(int m, int n, f32x4 v) const {
+  __device__ __forceinline__ void apply(int m, int n, f32x4 v, f32x4 cs) const {
     if (rscale) v *= rscale[m];
     int b = m / seqlen, s = m - b * seqlen;
     int pos = start_pos + s;
     if (n < nq) {
-      store4(q_out + (int64_t)m * nq + n, rope(v, pos, n % head_dim));
+      store4(q_out + (int64_t)m * nq + n, rotate(v, cs));
     } else if (n < nq + nkv) {
       int c = n - nq;
-      store4(cache_k + ((int64_t)b * max_seq + pos) * nkv + c, rope(v, pos, c % head_dim));
+      store4(cache_k + ((int64_t)b * max_seq + pos) * nkv + c, rotate(v, cs));
     } else {
       int c = n - nq - nkv;
       store4(cache_v + ((int64_t)b * max_seq + pos) * nkv + c, v);
     }
   }
+  __device__ __forceinline__ void operator()(int m, int n, f32x4 v) const { apply(m, n, v, cos_sin(m, n)); }
 };
+
+// Row-hoisted, two-phase form of an epilogue for the GEMM kernels.  epi_row(m)
+// computes what depends on the row only (once per row fragment); epi_pre(row,
+// n) loads what the group of columns n..n+3 needs (the QKV epilogue's (cos,
+// sin)), fetched for a whole fragment before its stores, which the compiler
+// could not otherwise move the loads past (the pointers may alias); epi_apply
+// finishes the group.  Plain epilogues take the row index and load nothing.
+struct NoPre {};
+template <class Epi>
+__device__ __forceinline__ int epi_row(const Epi&, int m) {
+  return m;
+}
+template <class Epi>
+__device__ __forceinline__ NoPre epi_pre(const Epi&, int, int) {
+  return {};
+}
+template <class Epi>
+__device__ __forceinline__ void epi_apply(const Epi& e, int m, int n, f32x4 v, NoPre) {
+  e(m, n, v);
+}
+
+template <typename T>
+struct QkvRow {
+  T* q;              // q_out row
+  T* k;              // cache_k row at the token's position
+  T* v;              // cache_v row
+  const float* cs;   // (cos, sin) table row of the position
+  float scale;       // RMSNorm factor (1 without)
+};
+template <typename T>
+__device__ __forceinline__ QkvRow<T> epi_row(const EpiQKV<T>& e, int m) {
+  const int b = m / e.seqlen, s = m - b * e.seqlen;
+  const int pos = e.start_pos + s;
+  const int64_t crow = ((int64_t)b * e.max_seq + pos) * e.nkv;
+  return QkvRow<T>{e.q_out + (int64_t)m * e.nq, e.cache_k + crow, e.cache_v + crow,
+                   e.freqs + (int64_t)pos * e.head_dim, e.rscale ? e.rscale[m] : 1.0f};
+}
+template <typename T>
+__device__ __forceinline__ f32x4 epi_pre(const EpiQKV<T>& e, const QkvRow<T>& r, int n) {
+  const int c = n < e.nq ? n : n - e.nq;   // v columns load a harmless table entry
+  return *(const f32x4*)(r.cs + (c & (e.head_dim - 1)));
+}
+template <typename T>
+__device__ __forceinline__ void epi_apply(const EpiQKV<T>& e, const QkvRow<T>& r, int n, f32x4 v, f32x4 cs) {
+  v *= r.scale;
+  const bool is_q = n < e.nq, is_v = n >= e.nq + e.nkv;
+  const f32x4 o = is_v ? v : EpiQKV<T>::rotate(v, cs);
+  T* dst = is_q ? r.q + n : (is_v ? r.v + (n - e.nq - e.nkv) : r.k + (n - e.nq));
+  store4(dst, o);
+}
 
 // SwiGLU epilogue: g = silu(a1) * a3 with a1 = (x w1^T), a3 = (x w3^T).
 template <typename T>
