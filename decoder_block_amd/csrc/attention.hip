@@ -28,6 +28,8 @@
 // f32: one wavefront per (b, s, h) with scalar online softmax (small shapes).
 #include "attention.hpp"
 
+#include <type_traits>
+
 #include <math.h>
 
 namespace llama {
@@ -161,20 +163,34 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
   const bf16* kbase = ck + ((int64_t)b * sh.max_seq * Hkv + j) * HD;
   const bf16* vbase = cv + ((int64_t)b * sh.max_seq * Hkv + j) * HD;
 
-  // DMA of key tile t0 into ring slot st: block (wave*DMA + i) holds keys
-  // KPB*(wave*DMA + i) .. +KPB; lane l fetches key + l/CHK, chunk (l%CHK) ^ swz(key)
-  auto issue = [&](int t0, int st) {
+  // DMA of key tile t0 into ring slot ST: block (wave*DMA + i) holds keys
+  // KPB*(wave*DMA + i) .. +KPB; lane l fetches key + l/CHK, chunk (l%CHK) ^ swz(key).
+  // Per-lane parts are computed once: 32-bit byte offsets from the sequence's
+  // cache base (one sequence's rows stay below 2^31 elements, checked on the
+  // host) and the chunk swizzles; a tile adds its first key.
+  const char* kb8 = (const char*)kbase;
+  const char* vb8 = (const char*)vbase;
+  const uint32_t stride_b = (uint32_t)stride * 2;
+  int dkey[DMA];
+  uint32_t dk_off[DMA], dv_off[DMA];
+#pragma unroll
+  for (int i = 0; i < DMA; ++i) {
+    const int key = (wave * DMA + i) * KPB + lane / CHK;
+    dkey[i] = key;
+    dk_off[i] = (uint32_t)(((lane % CHK) ^ kswz(key)) * 16);
+    dv_off[i] = (uint32_t)(((lane % CHK) ^ vswz(key)) * 16);
+  }
+  auto issue = [&](int t0, auto st_c) {
+    constexpr int ST = decltype(st_c)::value;
+    const bool full = t0 + BKV <= kend;          // no key of the tile past the end: no clamp
 #pragma unroll
     for (int i = 0; i < DMA; ++i) {
-      const int blk = wave * DMA + i;
-      const int key = blk * KPB + lane / CHK;
-      const int t = min(t0 + key, kend - 1);
-      const int ckk = (lane % CHK) ^ kswz(key);
-      const int cvv = (lane % CHK) ^ vswz(key);
-      __builtin_amdgcn_global_load_lds((const void*)(kbase + t * stride + ckk * 8),
-                                       (LLAMA_LDS void*)&Ks[st][blk * 64], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vbase + t * stride + cvv * 8),
-                                       (LLAMA_LDS void*)&Vs[st][blk * 64], 16, 0, 0);
+      const int t = full ? t0 + dkey[i] : min(t0 + dkey[i], kend - 1);
+      const uint32_t row = (uint32_t)t * stride_b;
+      __builtin_amdgcn_global_load_lds((const void*)(kb8 + (row + dk_off[i])),
+                                       (LLAMA_LDS void*)&Ks[ST][(wave * DMA + i) * 64], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vb8 + (row + dv_off[i])),
+                                       (LLAMA_LDS void*)&Vs[ST][(wave * DMA + i) * 64], 16, 0, 0);
     }
   };
 
@@ -182,28 +198,41 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
 #pragma unroll
   for (int i = 0; i < HD / 32; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
+  // Fragment addresses, per lane, for slot 0 and key sub-tile 0; the slot, the
+  // sub-tile and the second 8 keys of a V^T read are immediate offsets.  The
+  // swizzles depend only on the key's low bits, which the sub-tile offsets
+  // (multiples of 8 keys) leave unchanged.
+  const bf16x8* kfp[HD / 16];
+#pragma unroll
+  for (int kk = 0; kk < HD / 16; ++kk) {
+    const int c = kk * 2 + lhalf;
+    kfp[kk] = &Ks[0][lrow * CHK + (c ^ kswz(lrow))];
+  }
   // V^T read: lane group g = lane/16 covers d0 = (g&1)*16 (+32*dt), keys base + hf*4 (+8)
   const int li = lane & 15;
   const int vkey_off = lhalf * 4 + (li >> 2);
   const int vd_off = ((lane >> 4) & 1) * 16 + (li & 3) * 4;
+  const bf16* vtp[HD / 32];
+#pragma unroll
+  for (int dt = 0; dt < HD / 32; ++dt) {
+    const int d = dt * 32 + vd_off;
+    vtp[dt] = (const bf16*)&Vs[0][vkey_off * CHK + ((d >> 3) ^ vswz(vkey_off))] + (d & 7);
+  }
 
-  issue(0, 0);
-  for (int it = 0; it < ntiles; ++it) {
-    const int st = it & 1;
+  auto tile = [&](int it, auto st_c) {
+    constexpr int ST = decltype(st_c)::value;
     const int t0 = it * BKV;
     attn_wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (it + 1 < ntiles) issue(t0 + BKV, st ^ 1);
+    if (it + 1 < ntiles) issue(t0 + BKV, std::integral_constant<int, ST ^ 1>{});
 
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const int key = kt * 32 + lrow;
 #pragma unroll
       for (int kk = 0; kk < HD / 16; ++kk) {
-        const int c = kk * 2 + lhalf;
-        const bf16x8 kf = Ks[st][key * CHK + (c ^ kswz(key))];
+        const bf16x8 kf = kfp[kk][ST * BKV * CHK + kt * 32 * CHK];
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[kt], 0, 0, 0);
       }
     }
@@ -251,21 +280,25 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        const int key0 = kt * 32 + h2 * 16 + vkey_off;
 #pragma unroll
         for (int dt = 0; dt < HD / 32; ++dt) {
-          const int d = dt * 32 + vd_off;
-          const int k1 = key0, k2 = key0 + 8;
-          const bf16* v1 = (const bf16*)&Vs[st][k1 * CHK + ((d >> 3) ^ vswz(k1))] + (d & 7);
-          const bf16* v2 = (const bf16*)&Vs[st][k2 * CHK + ((d >> 3) ^ vswz(k2))] + (d & 7);
+          const bf16* v1 = vtp[dt] + (ST * BKV + kt * 32 + h2 * 16) * CHK * 8;
           const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LLAMA_LDS bf16x4_t*)v1);
-          const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LLAMA_LDS bf16x4_t*)v2);
-          const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LLAMA_LDS bf16x4_t*)(v1 + 8 * CHK * 8));
+          const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kt][h2], oacc[dt], 0, 0, 0);
         }
       }
     asm volatile("" ::: "memory");
+  };
+
+  issue(0, std::integral_constant<int, 0>{});
+  int it = 0;
+  for (; it + 1 < ntiles; it += 2) {
+    tile(it, std::integral_constant<int, 0>{});
+    tile(it + 1, std::integral_constant<int, 1>{});
   }
+  if (it < ntiles) tile(it, std::integral_constant<int, 0>{});
 
   if (!row_valid) return;
   const float inv = 1.0f / l_run;
