@@ -413,27 +413,34 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
       }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = exp2f(m_run - m_new);
+    // lazy rescale: the running max moves only when some head's max grows by
+    // more than 8 (probabilities then stay below 2^8); the result is unchanged
+    if (__any(mloc > m_run + 8.0f)) {
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < HD / 16; ++dt) oacc[dt] *= alpha;
+      m_run = m_new;
+    }
     float psum = 0.f;
     bf16x8 pf;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        float p = exp2f(sacc[kt][v] - m_new);
+        float p = __builtin_amdgcn_exp2f(sacc[kt][v] - m_run);
         psum += p;
         pf[kt * 4 + v] = (bf16)p;
       }
     psum += __shfl_xor(psum, 16, 64);
     psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    l_run += psum;
 #pragma unroll
     for (int dt = 0; dt < HD / 16; ++dt) {
       const int d = dt * 16 + l16;
       bf16x8 vf = Vt[wave][d * 4 + (g ^ ((d >> 2) & 3))];
-      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[dt] * alpha, 0, 0, 0);
+      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[dt], 0, 0, 0);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
