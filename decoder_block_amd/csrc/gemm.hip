@@ -25,8 +25,12 @@ constexpr int kBigBK = 64;
 constexpr int kBigStages = 2;
 constexpr int kBigWaves = 8;
 constexpr int kCUs = 256;         // MI355X compute units
-constexpr int kSkinnyBK = 64;     // small M: 128-byte row pieces per k-tile
-constexpr int kSkinnyStages = 4;  // small M: ring depth (4 x 40 KiB fills the LDS)
+// small M (<= 64 tokens: the weights stream from HBM once): 64-deep k-tiles
+// (128-byte row pieces).  Tiles: M <= 32: 32 rows x 128 columns in a 6-stage
+// ring, 32 x 256 for the dual w1/w3 kernel (4 stages); 33..64 rows: 64 x 128,
+// 6 stages.  Narrow tiles need fewer K-splits to cover the CUs (measured:
+// LLaMA-3-8B-shaped w1/w3 at M = 64 went from 70 to 48 us).
+constexpr int kSkinnyBK = 64;
 
 template <typename T>
 __device__ __forceinline__ const T* weight_row(const WeightRows<T>& w, int n, int K) {
@@ -259,7 +263,7 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
   constexpr int MF = TN * TM;                 // MFMAs per half
   static_assert(BK == 32 || BK == 64, "BK");
   static_assert(NS >= 2 && BLOCKS % NW == 0 && TM >= 1 && TN >= 1 && (!DUAL || TN % 2 == 0), "shape");
-  static_assert(MF >= RD && WAVES_M * WAVES_N == NW, "interleave");
+  static_assert(WAVES_M * WAVES_N == NW, "waves");
   __shared__ bf16x8 smem[NS][ROWS * CH];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -339,14 +343,13 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
         acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
   };
   // the RD fragment reads for the next step go out one after each of the first
-  // RD MFMAs, leaving the last MF - RD MFMAs to cover their latency
+  // MFMAs, leaving the last MF - RD MFMAs (if any) to cover their latency
   auto interleave = [&]() {
 #pragma unroll
-    for (int i = 0; i < RD; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int i = 0; i < (MF > RD ? MF : RD); ++i) {
+      if (i < MF) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    if constexpr (MF > RD) __builtin_amdgcn_sched_group_barrier(0x008, MF - RD, 0);
   };
 
   constexpr int KS = BK / 16;                 // 16-deep MFMA steps per k-tile
@@ -615,8 +618,15 @@ hipError_t launch_bf16(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, in
                        int splits, float* partial, hipStream_t st) {
   // the DMA-pipelined kernels need K (and each split's K range) in whole k-tiles
   // (BK = kSkinnyBK for small M, kBigBK otherwise) and 16-byte aligned rows
-  if (lda % 8 == 0 && M <= 64 && K % kSkinnyBK == 0)
-    return launch_dma<64, 256, kSkinnyBK, 1, kSkinnyStages, DUAL, 4>(A, lda, w, M, N, K, epi, splits, partial, st);
+  if (lda % 8 == 0 && M <= 64 && K % kSkinnyBK == 0) {
+    if (M <= 32) {
+      if constexpr (DUAL)
+        return launch_dma<32, 256, kSkinnyBK, 1, 4, DUAL, 4>(A, lda, w, M, N, K, epi, splits, partial, st);
+      else
+        return launch_dma<32, 128, kSkinnyBK, 1, 6, DUAL, 4>(A, lda, w, M, N, K, epi, splits, partial, st);
+    }
+    return launch_dma<64, 128, kSkinnyBK, 2, 6, DUAL, 4>(A, lda, w, M, N, K, epi, splits, partial, st);
+  }
   if (lda % 8 == 0 && M > 64 && K % kBigBK == 0 && splits <= 1)
     return launch_dma<256, 256, kBigBK, 2, kBigStages, DUAL, kBigWaves>(A, lda, w, M, N, K, epi, 1, partial, st);
   hipError_t e;
@@ -657,13 +667,16 @@ int gemm_pick_splits(int M, int N, int K, bool dual, bool is_bf16) {
   // small token count: the weights stream from HBM once; split K so that the
   // grid covers the CUs
   if (is_bf16 && K % kSkinnyBK == 0) {
-    // LDS-DMA kernel: its ring fills a CU's LDS, so one workgroup per CU; aim at
-    // one wave of workgroups (fewer splits measured faster than oversubscribing:
-    // every split adds an fp32 partial tile and shortens the pipeline)
-    const int tiles = (N + (dual ? 127 : 255)) / (dual ? 128 : 256);
+    // LDS-DMA kernel: its ring fills most of a CU's LDS, so one workgroup per CU;
+    // aim at one wave of workgroups (fewer splits measured faster than
+    // oversubscribing: every split adds an fp32 partial tile and shortens the
+    // pipeline), each split keeping at least a ring's depth of k-tiles
+    const int bn_out = dual ? (M <= 32 ? 128 : 64) : 128;
+    const int stages = (dual && M <= 32) ? 4 : 6;
+    const int tiles = (N + bn_out - 1) / bn_out;
     const int nkt = K / kSkinnyBK;
     int s = tiles >= kCUs ? 1 : kCUs / tiles;
-    s = min(s, max(1, nkt / kSkinnyStages));
+    s = min(s, max(1, nkt / stages));
     // every split must own at least one k-tile: use the count the rounding yields
     const int per = (nkt + s - 1) / s;
     return (nkt + per - 1) / per;
