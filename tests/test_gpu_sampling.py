@@ -128,3 +128,17 @@ def test_equal_logits_many_ties():
         np.testing.assert_array_equal(got, np.floor(u * kept).astype(np.int64))
         np.testing.assert_array_equal(got, osm.sample(lg, 1.0, p, u))
     np.testing.assert_array_equal(_run(lg, 1.0, 1.0, u), np.floor(u * V).astype(np.int64))
+
+
+def test_equal_logits_full_vocab_fallback():
+    """128256 equal logits: every token stays in the search range, more than the
+    candidate list holds, so the selection keeps reading the row; the result is
+    still the closed form floor(u * kept)."""
+    need_gpu()
+    print("case sample equal logits, 128256 tokens", flush=True)
+    V = 128256
+    lg = np.full((2, V), -1.5, dtype=np.float32)
+    u = np.array([0.1234, 0.87], dtype=np.float32).astype(np.float64)
+    p = 0.61234                                         # p * V = 78536.4...
+    kept = int(np.floor(p * V)) + 1
+    np.testing.assert_array_equal(_run(lg, 1.0, p, u), np.floor(u * kept).astype(np.int64))
