@@ -326,11 +326,16 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
   const int H = sh.n_heads, Hkv = sh.n_kv_heads;
   const int n_rep = H / Hkv;
   const int hgs = (n_rep + 15) / 16;
-  // grid x walks the kv heads fastest: the workgroups that share each cache
-  // row (one 2*head_dim-byte piece per kv head) are dispatched together
-  const int j = blockIdx.x / hgs, hg = blockIdx.x % hgs;
-  const int z = blockIdx.y;
-  const int b = blockIdx.z;
+  // grid x walks the kv heads fastest, and the flattened workgroup id is
+  // remapped so that consecutive ids share an XCD: the workgroups that read the
+  // pieces of the same cache rows (2*head_dim bytes per kv head) run together
+  // on one XCD instead of being dealt round-robin over all eight
+  const int nbx = gridDim.x, nby = gridDim.y;
+  const int lid = xcd_remap(blockIdx.x + nbx * (blockIdx.y + nby * blockIdx.z), nbx * nby * gridDim.z);
+  const int bx = lid % nbx, by = (lid / nbx) % nby;
+  const int j = bx / hgs, hg = bx % hgs;
+  const int z = by;
+  const int b = lid / (nbx * nby);
   const int T = sh.start_pos + 1;
   const int t_begin = z * L, t_end = min(T, t_begin + L);
 
