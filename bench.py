@@ -207,6 +207,24 @@ def bench_stack(dev, steps):
     pre = e[0].elapsed_time(e[1])
     dec = e[1].elapsed_time(e[2]) / steps
     log(f"stack prefill {pre:.1f} ms, decode {dec:.3f} ms/step")
+    # the same steps replayed from one captured HIP graph (position held on the device)
+    stack.forward(prompt, 0, logits, out[0])
+    tok = out[0].clone()
+    pos = torch.full((1,), w.prefill_len, dtype=torch.int32, device=dev)
+    max_pos = w.prefill_len + steps
+    stack.decode_step_at(tok, pos, max_pos, logits)      # eager first step (loads the kernels)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        stack.decode_step_at(tok, pos, max_pos, logits)
+    torch.cuda.synchronize()
+    e[0].record()
+    for _ in range(steps):
+        graph.replay()
+    e[1].record()
+    torch.cuda.synchronize()
+    dec_g = e[0].elapsed_time(e[1]) / steps
+    log(f"stack decode from a HIP graph {dec_g:.3f} ms/step")
+    del graph
     # top-p sampling of the last step's logits (temperature 0.8, top_p 0.95: the walkthrough's defaults)
     g = torch.Generator(device=dev).manual_seed(5)
     uni = torch.rand(20, w.batch, generator=g, device=dev)
@@ -222,6 +240,7 @@ def bench_stack(dev, steps):
     samp = s0.elapsed_time(s1) / 20
     res = {"prefill_ms": round(pre, 2), "prefill_tokens_per_s": round(w.batch * w.prefill_len / pre * 1e3, 1),
            "decode_ms_per_step": round(dec, 3), "decode_tokens_per_s": round(w.batch / dec * 1e3, 1),
+           "graph_decode_ms_per_step": round(dec_g, 3), "graph_decode_tokens_per_s": round(w.batch / dec_g * 1e3, 1),
            "decode_steps_timed": steps, "batch": w.batch, "prompt": w.prefill_len, "layers": w.n_layers,
            "top_p_sampling_us": round(samp * 1e3, 1)}
     del stack

@@ -28,7 +28,8 @@ EXPORTS = (
     "llama_status_str", "llama_ffn_hidden_dim", "llama_block_workspace_size",
     "llama_attn_decode_workspace_size", "llama_ffn_workspace_size", "llama_rope_freqs",
     "llama_rmsnorm", "llama_rope", "llama_gqa_attn_prefill", "llama_gqa_attn_decode",
-    "llama_swiglu_ffn", "llama_linear", "llama_block_forward", "llama_block_forward_events", "llama_embedding",
+    "llama_swiglu_ffn", "llama_linear", "llama_block_forward", "llama_block_forward_events",
+    "llama_block_decode_at", "llama_embedding",
     "llama_lm_head_workspace_size", "llama_lm_head_argmax", "llama_sample_top_p",
 )
 
@@ -103,6 +104,8 @@ def lib() -> ctypes.CDLL:
                                      ctypes.c_int, P], ctypes.c_int),
             "llama_block_forward_events": ([A, ctypes.POINTER(CBlockWeights), P, P, P, I32, P, P, I32, I32, I32, P,
                                             SZ, ctypes.c_int, P, ctypes.POINTER(P)], ctypes.c_int),
+            "llama_block_decode_at": ([A, ctypes.POINTER(CBlockWeights), P, P, P, I32, P, P, I32, P, I32, P, SZ,
+                                       ctypes.c_int, P], ctypes.c_int),
             "llama_embedding": ([P, P, P, I64, I32, I32, ctypes.c_int, P], ctypes.c_int),
             "llama_lm_head_argmax": ([P, I64, P, P, P, P, I32, I32, I32, F, P, SZ, ctypes.c_int, P], ctypes.c_int),
             "llama_sample_top_p": ([P, P, I32, I32, F, F, P, P], ctypes.c_int),
@@ -233,6 +236,16 @@ def llama_block_forward(args: ModelArgs, weights, cache_k, cache_v, freqs, freqs
     _check(lib().llama_block_forward(ctypes.byref(args.c()), ctypes.byref(w), _ptr(cache_k), _ptr(cache_v),
                                      _ptr(freqs), freqs_end, _ptr(x), _ptr(out), bsz, seqlen, start_pos, _ptr(ws),
                                      ws_bytes, _dtype(x), _stream(stream)), "llama_block_forward")
+
+
+def llama_block_decode_at(args: ModelArgs, weights, cache_k, cache_v, freqs, freqs_end: int, x, out, bsz: int,
+                          start_pos_dev, max_start_pos: int, ws, ws_bytes: int, stream=None) -> None:
+    """One-token block decode at the position held in ``start_pos_dev`` (device int32)."""
+    w = weights if isinstance(weights, CBlockWeights) else block_weights(weights)
+    _check(lib().llama_block_decode_at(ctypes.byref(args.c()), ctypes.byref(w), _ptr(cache_k), _ptr(cache_v),
+                                       _ptr(freqs), freqs_end, _ptr(x), _ptr(out), bsz, _ptr(start_pos_dev),
+                                       max_start_pos, _ptr(ws), ws_bytes, _dtype(x), _stream(stream)),
+           "llama_block_decode_at")
 
 
 def llama_block_forward_events(args: ModelArgs, weights, cache_k, cache_v, freqs, freqs_end: int, x, out, bsz: int,

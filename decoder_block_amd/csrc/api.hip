@@ -118,7 +118,9 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 template <typename T>
 int block_forward_t(const Dims& g, const llama_model_args* a, const llama_block_weights* w, T* ck, T* cv,
                     const float* freqs, const T* x, T* out, int bsz, int seqlen, int start_pos, char* ws,
-                    const BlockWs& L, hipStream_t st, hipEvent_t* ev) {
+                    const BlockWs& L, hipStream_t st, hipEvent_t* ev, const int32_t* pos_dev) {
+  // pos_dev (optional, one-token bf16 calls): the position is read on the device,
+  // start_pos is then its upper bound
   // ev (optional): ev[0] before the first stage, ev[i] after stage i (i = 1..7)
   auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
   if (mark(0) != hipSuccess) return LLAMA_ERR_HIP;
@@ -143,14 +145,14 @@ int block_forward_t(const Dims& g, const llama_model_args* a, const llama_block_
   if (e != hipSuccess || mark(1) != hipSuccess) return LLAMA_ERR_HIP;
   {
     llama::WeightRows<T> wr{(const T*)w->wq, (const T*)w->wk, (const T*)w->wv, nq, nq + nkv};
-    llama::EpiQKV<T> epi{q, ck, cv, freqs, seqlen, start_pos, a->max_seq_len, nq, nkv, g.d, r1};
+    llama::EpiQKV<T> epi{q, ck, cv, freqs, seqlen, start_pos, a->max_seq_len, nq, nkv, g.d, r1, pos_dev};
     const int N = nq + 2 * nkv;
     e = llama::gemm_launch<T>(xn, g.D, wr, M, N, g.D, epi, llama::gemm_pick_splits(M, N, g.D, false, bf), part, st);
     if (e != hipSuccess || mark(2) != hipSuccess) return LLAMA_ERR_HIP;
   }
   llama::AttnShape sh{bsz, seqlen, start_pos, g.H, g.Hkv, g.d, a->max_seq_len};
   if (seqlen == 1)
-    e = llama::attn_decode<T>(q, ck, cv, o, sh, part, st);
+    e = llama::attn_decode<T>(q, ck, cv, o, sh, part, st, pos_dev);
   else
     e = llama::attn_prefill<T>(q, ck, cv, o, sh, st);
   if (e != hipSuccess || mark(3) != hipSuccess) return LLAMA_ERR_HIP;
@@ -404,7 +406,7 @@ int llama_swiglu_ffn(const void* x, const void* w1, const void* w3, const void* 
 static int block_forward_impl(const llama_model_args* a, const llama_block_weights* w, void* cache_k, void* cache_v,
                               const float* freqs, int32_t freqs_end, const void* x, void* out, int32_t bsz,
                               int32_t seqlen, int32_t start_pos, void* ws, size_t ws_bytes, llama_dtype dt,
-                              llama_stream_t stream, hipEvent_t* ev) {
+                              llama_stream_t stream, hipEvent_t* ev, const int32_t* pos_dev = nullptr) {
   Dims g;
   int rc = model_dims(a, dt, &g);
   if (rc != LLAMA_OK) return rc;
@@ -424,9 +426,9 @@ static int block_forward_impl(const llama_model_args* a, const llama_block_weigh
   hipStream_t st = (hipStream_t)stream;
   if (dt == LLAMA_BF16)
     return block_forward_t<bf16>(g, a, w, (bf16*)cache_k, (bf16*)cache_v, freqs, (const bf16*)x, (bf16*)out, bsz,
-                                 seqlen, start_pos, (char*)ws, L, st, ev);
+                                 seqlen, start_pos, (char*)ws, L, st, ev, pos_dev);
   return block_forward_t<float>(g, a, w, (float*)cache_k, (float*)cache_v, freqs, (const float*)x, (float*)out, bsz,
-                                seqlen, start_pos, (char*)ws, L, st, ev);
+                                seqlen, start_pos, (char*)ws, L, st, ev, nullptr);
 }
 
 int llama_block_forward(const llama_model_args* a, const llama_block_weights* w, void* cache_k, void* cache_v,
@@ -445,6 +447,16 @@ int llama_block_forward_events(const llama_model_args* a, const llama_block_weig
     if (!events[i]) return LLAMA_ERR_INVALID_ARG;
   return block_forward_impl(a, w, cache_k, cache_v, freqs, freqs_end, x, out, bsz, seqlen, start_pos, ws, ws_bytes,
                             dt, stream, (hipEvent_t*)events);
+}
+
+int llama_block_decode_at(const llama_model_args* a, const llama_block_weights* w, void* cache_k, void* cache_v,
+                          const float* freqs, int32_t freqs_end, const void* x, void* out, int32_t bsz,
+                          const int32_t* start_pos_dev, int32_t max_start_pos, void* ws, size_t ws_bytes,
+                          llama_dtype dt, llama_stream_t stream) {
+  if (!start_pos_dev || ((uintptr_t)start_pos_dev) % 4) return LLAMA_ERR_INVALID_ARG;
+  if (dt != LLAMA_BF16) return LLAMA_ERR_UNSUPPORTED;
+  return block_forward_impl(a, w, cache_k, cache_v, freqs, freqs_end, x, out, bsz, 1, max_start_pos, ws, ws_bytes,
+                            dt, stream, nullptr, start_pos_dev);
 }
 
 int llama_embedding(const int32_t* tokens, const void* table, void* out, int64_t n, int32_t dim, int32_t vocab,

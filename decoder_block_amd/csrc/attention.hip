@@ -317,7 +317,7 @@ template <int HD>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const bf16* __restrict__ cv,
                  bf16* __restrict__ out, float* __restrict__ partial, AttnShape sh, int nsplit, int L,
-                 float scale_log2) {
+                 float scale_log2, const int32_t* __restrict__ pos_dev) {
   constexpr int CH = HD / 8;
   static_assert(HD == 64 || HD == 128, "head_dim");
   __shared__ bf16x8 Vt[4][HD * 4];          // per wave: [d][4 chunks of 8 permuted keys]
@@ -336,7 +336,9 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
   const int j = bx / hgs, hg = bx % hgs;
   const int z = by;
   const int b = lid / (nbx * nby);
-  const int T = sh.start_pos + 1;
+  // (a device-resident position may leave the last splits without keys: they
+  // write an empty partial, max -inf and sum 0, which the combine weighs 0)
+  const int T = (pos_dev ? min(max(*pos_dev, 0), sh.start_pos) : sh.start_pos) + 1;
   const int t_begin = z * L, t_end = min(T, t_begin + L);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -622,7 +624,7 @@ int attn_decode_splits(int bsz, int n_heads, int n_kv_heads, int T) {
 
 template <typename T>
 hipError_t attn_decode(const T* q, const T* cache_k, const T* cache_v, T* out, const AttnShape& sh,
-                       float* partial, hipStream_t st) {
+                       float* partial, hipStream_t st, const int32_t* pos_dev) {
   const float scale = 1.0f / sqrtf((float)sh.head_dim);
   if constexpr (sizeof(T) == 2) {
     const int T_ = sh.start_pos + 1;
@@ -632,13 +634,16 @@ hipError_t attn_decode(const T* q, const T* cache_k, const T* cache_v, T* out, c
     const int n_rep = sh.n_heads / sh.n_kv_heads;
     dim3 grid(sh.n_kv_heads * ((n_rep + 15) / 16), ns, sh.bsz);
     if (sh.head_dim == 128)
-      attn_decode_mfma<128><<<grid, 256, 0, st>>>(q, cache_k, cache_v, out, partial, sh, ns, L, scale * kLog2e);
+      attn_decode_mfma<128><<<grid, 256, 0, st>>>(q, cache_k, cache_v, out, partial, sh, ns, L, scale * kLog2e,
+                                                  pos_dev);
     else
-      attn_decode_mfma<64><<<grid, 256, 0, st>>>(q, cache_k, cache_v, out, partial, sh, ns, L, scale * kLog2e);
+      attn_decode_mfma<64><<<grid, 256, 0, st>>>(q, cache_k, cache_v, out, partial, sh, ns, L, scale * kLog2e,
+                                                 pos_dev);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1) return e;
     attn_decode_combine<T><<<sh.bsz * sh.n_heads, 256, 0, st>>>(partial, out, ns, sh.head_dim);
   } else {
+    if (pos_dev) return hipErrorNotSupported;
     const int64_t waves = (int64_t)sh.bsz * sh.n_heads;
     attn_simple<T><<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(q, cache_k, cache_v, out, sh, scale);
   }
@@ -651,8 +656,8 @@ template hipError_t attn_prefill<bf16>(const bf16*, const bf16*, const bf16*, bf
 template hipError_t attn_prefill<float>(const float*, const float*, const float*, float*, const AttnShape&,
                                         hipStream_t);
 template hipError_t attn_decode<bf16>(const bf16*, const bf16*, const bf16*, bf16*, const AttnShape&, float*,
-                                      hipStream_t);
+                                      hipStream_t, const int32_t*);
 template hipError_t attn_decode<float>(const float*, const float*, const float*, float*, const AttnShape&,
-                                       float*, hipStream_t);
+                                       float*, hipStream_t, const int32_t*);
 
 }  // namespace llama

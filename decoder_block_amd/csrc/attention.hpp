@@ -25,10 +25,13 @@ hipError_t attn_prefill(const T* q, const T* cache_k, const T* cache_v, T* out,
                         const AttnShape& sh, hipStream_t st);
 
 // Decode (seqlen == 1): split-K over the T keys; `partial` holds
-// bsz * n_heads * splits * (head_dim + 2) floats.
+// bsz * n_heads * splits * (head_dim + 2) floats.  With pos_dev set (bf16
+// only), the position is *pos_dev, read when the kernel runs and clamped to
+// [0, sh.start_pos]; the splits are laid out for T = sh.start_pos + 1 and those
+// past the actual length stay empty.
 int attn_decode_splits(int bsz, int n_heads, int n_kv_heads, int T);
 template <typename T>
 hipError_t attn_decode(const T* q, const T* cache_k, const T* cache_v, T* out,
-                       const AttnShape& sh, float* partial, hipStream_t st);
+                       const AttnShape& sh, float* partial, hipStream_t st, const int32_t* pos_dev = nullptr);
 
 }  // namespace llama

@@ -54,7 +54,9 @@ struct EpiF32 {
 // get the interleaved-pair rotation of their position (start_pos + m % seqlen)
 // from the fp32 (cos, sin) table; q goes to q_out [M][nq]; k and v are written
 // straight into the caches at [b][start_pos + s] (cache append).  head_dim is a
-// power of two.
+// power of two.  With pos_dev set, the base position is *pos_dev, read when the
+// kernel runs and clamped to [0, start_pos] (start_pos then holds the largest
+// position the caller allows).
 template <typename T>
 struct EpiQKV {
   T* q_out;
@@ -63,10 +65,12 @@ struct EpiQKV {
   const float* freqs;  // [freqs_end][head_dim/2][2]
   int seqlen, start_pos, max_seq, nq, nkv, head_dim;
   const float* rscale; // optional per-row RMSNorm factor applied to the accumulators
+  const int32_t* pos_dev = nullptr;  // optional device-resident base position
+  __device__ __forceinline__ int base() const { return pos_dev ? min(max(*pos_dev, 0), start_pos) : start_pos; }
   // (cos_i, sin_i, cos_i+1, sin_i+1) of columns n..n+3 (zero for v columns)
   __device__ __forceinline__ f32x4 cos_sin(int m, int n) const {
     if (n >= nq + nkv) return f32x4{};
-    const int pos = start_pos + (m - (m / seqlen) * seqlen);
+    const int pos = base() + (m - (m / seqlen) * seqlen);
     const int e = (n < nq ? n : n - nq) & (head_dim - 1);
     return *(const f32x4*)(freqs + ((int64_t)pos * (head_dim >> 1) + (e >> 1)) * 2);
   }
@@ -77,7 +81,7 @@ struct EpiQKV {
   __device__ __forceinline__ void apply(int m, int n, f32x4 v, f32x4 cs) const {
     if (rscale) v *= rscale[m];
     int b = m / seqlen, s = m - b * seqlen;
-    int pos = start_pos + s;
+    int pos = base() + s;
     if (n < nq) {
       store4(q_out + (int64_t)m * nq + n, rotate(v, cs));
     } else if (n < nq + nkv) {
@@ -122,7 +126,7 @@ struct QkvRow {
 template <typename T>
 __device__ __forceinline__ QkvRow<T> epi_row(const EpiQKV<T>& e, int m) {
   const int b = m / e.seqlen, s = m - b * e.seqlen;
-  const int pos = e.start_pos + s;
+  const int pos = e.base() + s;
   const int64_t crow = ((int64_t)b * e.max_seq + pos) * e.nkv;
   return QkvRow<T>{e.q_out + (int64_t)m * e.nq, e.cache_k + crow, e.cache_v + crow,
                    e.freqs + (int64_t)pos * e.head_dim, e.rscale ? e.rscale[m] : 1.0f};

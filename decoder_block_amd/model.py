@@ -77,14 +77,45 @@ class StackRunner:
         L.llama_lm_head_argmax(last, seqlen * D, self.norm_w, self.w_out, logits, next_tok, bsz, D, self.vocab,
                                self.args.norm_eps, self.ws, ws_bytes)
 
+    def decode_step_at(self, tok: torch.Tensor, pos_dev: torch.Tensor, max_pos: int, logits: torch.Tensor,
+                       temperature: float = 0.0, top_p: float = 0.95, u: Optional[torch.Tensor] = None) -> None:
+        """One-token step at the position held on the device in ``pos_dev`` (int32 [1],
+        at most ``max_pos``): reads the ids in ``tok`` [bsz], overwrites them with the
+        chosen ids (argmax, or top-p with the uniforms in ``u`` [bsz] when the
+        temperature is positive) and advances ``pos_dev`` by one.  Every argument is
+        a fixed buffer and nothing is allocated once the workspace exists, so the
+        step can be captured in a HIP graph once and replayed position after
+        position."""
+        bsz = tok.shape[0]
+        ws_bytes = self._workspace(bsz, 1, max_pos)
+        a, b = self._acts(bsz, 1)
+        D = self.args.dim
+        L.llama_embedding(tok, self.embedding, a, bsz, D, self.vocab)
+        for layer in self.layers:
+            L.llama_block_decode_at(self.args, layer.cw, layer.cache_k, layer.cache_v, layer.freqs, layer.freqs_end,
+                                    a, b, bsz, pos_dev, max_pos, self.ws, ws_bytes)
+            a, b = b, a
+        L.llama_lm_head_argmax(a[:, 0], D, self.norm_w, self.w_out, logits, tok, bsz, D, self.vocab,
+                               self.args.norm_eps, self.ws, ws_bytes)
+        if temperature > 0:
+            L.llama_sample_top_p(logits, tok, bsz, self.vocab, temperature, top_p, u)
+        pos_dev.add_(1)
+
     def generate(self, prompt: torch.Tensor, steps: int, on_step=None, temperature: float = 0.0,
-                 top_p: float = 0.95, uniforms: Optional[torch.Tensor] = None) -> torch.Tensor:
+                 top_p: float = 0.95, uniforms: Optional[torch.Tensor] = None, graph: bool = False) -> torch.Tensor:
         """Generation: prefill the prompt, then ``steps`` one-token calls.
         Returns the generated ids [steps + 1, bsz]: row t is chosen on the device
         from call t's logits and is passed, as is, as the input ids of call t + 1
         (no host synchronisation inside the loop).  temperature 0 takes the argmax;
         a positive temperature samples with the nucleus cut top_p, call t drawing
-        with uniforms[t] ([steps + 1, bsz] floats in [0, 1), on the device)."""
+        with uniforms[t] ([steps + 1, bsz] floats in [0, 1), on the device).
+
+        graph=True runs the first one-token call eagerly, captures the next one
+        (embedding, every layer, final norm, output projection, token choice and
+        position advance) in a HIP graph and replays it for the rest; the position
+        lives on the device, and between replays only the chosen ids (and the
+        next uniforms) are copied on the device.  The results are those of
+        graph=False."""
         bsz, S = prompt.shape
         out = torch.empty(steps + 1, bsz, dtype=torch.int32, device=self.device)
         logits = torch.empty(bsz, self.vocab, dtype=torch.float32, device=self.device)
@@ -99,7 +130,33 @@ class StackRunner:
                 on_step(t, logits, out[t])
         self.forward(prompt, 0, logits, out[0])
         pick(0)
-        for t in range(steps):
-            self.forward(out[t].view(bsz, 1), S + t, logits, out[t + 1])
-            pick(t + 1)
+        if not graph:
+            for t in range(steps):
+                self.forward(out[t].view(bsz, 1), S + t, logits, out[t + 1])
+                pick(t + 1)
+            return out
+        if steps == 0:
+            return out
+        max_pos = S + steps - 1
+        tok = out[0].clone()
+        pos = torch.full((1,), S, dtype=torch.int32, device=self.device)
+        u = torch.empty(bsz, dtype=torch.float32, device=self.device) if sampled else None
+
+        def run_step(t, replay):
+            if sampled:
+                u.copy_(uniforms[t])
+            if replay is None:
+                self.decode_step_at(tok, pos, max_pos, logits, temperature, top_p, u)
+            else:
+                replay.replay()
+            out[t].copy_(tok)
+            if on_step is not None:
+                on_step(t, logits, out[t])
+        run_step(1, None)                      # eager: also loads every kernel before the capture
+        if steps > 1:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.decode_step_at(tok, pos, max_pos, logits, temperature, top_p, u)
+            for t in range(2, steps + 1):
+                run_step(t, g)
         return out

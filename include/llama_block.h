@@ -212,6 +212,29 @@ int llama_block_forward_events(const llama_model_args* args, const llama_block_w
                                int32_t seqlen, int32_t start_pos, void* ws, size_t ws_bytes,
                                llama_dtype dtype, llama_stream_t stream, void* const* events);
 
+/* One-token decode of the block at a position held in device memory (the
+ * generate loop of the linkmax.top walkthrough, section 3.3, feeds each new
+ * token back at start_pos + 1): identical to llama_block_forward with
+ * seqlen = 1 and start_pos = *start_pos_dev, except that the position is read
+ * by the kernels when they execute, so one recorded call (e.g. in a captured
+ * HIP graph) can be replayed at successive positions by advancing
+ * *start_pos_dev on the device between replays.
+ *   start_pos_dev: device int32, 4-byte aligned, shared by all bsz rows.
+ *   max_start_pos: the largest position the call may see.  The host validates
+ *     max_start_pos + 1 <= max_seq_len and <= freqs_end, and sizes the
+ *     workspace and the attention splits for it: ws_bytes >=
+ *     llama_block_workspace_size(args, bsz, 1, max_start_pos, dtype).
+ *   The caller guarantees 0 <= *start_pos_dev <= max_start_pos when the call
+ *   runs; the kernels clamp the value into that range (so memory accesses stay
+ *   inside the caches) but cannot report a violation.
+ * bf16 only (LLAMA_ERR_UNSUPPORTED for fp32); other arguments and errors as
+ * llama_block_forward. */
+int llama_block_decode_at(const llama_model_args* args, const llama_block_weights* weights,
+                          void* cache_k, void* cache_v, const float* freqs_cis, int32_t freqs_end,
+                          const void* x, void* out, int32_t bsz, const int32_t* start_pos_dev,
+                          int32_t max_start_pos, void* ws, size_t ws_bytes, llama_dtype dtype,
+                          llama_stream_t stream);
+
 /* Token embedding lookup (notes, section 3, Transformer.forward, tok_embeddings):
  * out[i] = table[tokens[i]].  tokens: device int32 [n]; table: device [vocab][dim];
  * out: device [n][dim].  Ids outside [0, vocab) produce a zero row (checked on the

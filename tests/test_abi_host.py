@@ -150,3 +150,34 @@ def test_device_entry_points_reject_bad_arguments():
     assert lib.llama_sample_top_p(p, p, 4, 100, float("nan"), 0.9, p, None) == E       # temperature NaN
     assert lib.llama_sample_top_p(p, p, 4, 100, 0.8, 0.9, None, None) == E             # sampling needs uniforms
     assert lib.llama_lm_head_argmax(p, 100, p, p, p, p, 2, 256, 1000, 1e-5, p, 1 << 30, dba.LLAMA_BF16, None) == E
+
+
+def _raw_decode_at(a, **over):
+    """Call llama_block_decode_at through ctypes with dummy non-null pointers."""
+    lib = dba.lib()
+    fake = 1 << 20
+    kw = dict(bsz=1, pos=fake * 4, max_pos=0, freqs_end=16, ws_bytes=0, dtype=dba.LLAMA_BF16, x=fake,
+              out=fake * 2, ck=fake, cv=fake, freqs=fake, ws=fake)
+    kw.update(over)
+    w = L.CBlockWeights(*([fake] * 9))
+    return lib.llama_block_decode_at(ctypes.byref(a.c()), ctypes.byref(w), kw["ck"], kw["cv"], kw["freqs"],
+                                     kw["freqs_end"], kw["x"], kw["out"], kw["bsz"], kw["pos"], kw["max_pos"],
+                                     kw["ws"], kw["ws_bytes"], kw["dtype"], None)
+
+
+def test_block_decode_at_validation_errors():
+    """The device-position decode validates against max_start_pos on the host."""
+    a = dba.ModelArgs(dim=256, n_heads=2, n_kv_heads=1, max_batch_size=2, max_seq_len=16)
+    E, U, W = dba._lib.LLAMA_ERR_INVALID_ARG, dba._lib.LLAMA_ERR_UNSUPPORTED, dba._lib.LLAMA_ERR_WORKSPACE_TOO_SMALL
+    assert _raw_decode_at(a) == W                            # valid call, workspace missing
+    assert _raw_decode_at(a, max_pos=15) == W                # the last cache row
+    assert _raw_decode_at(a, max_pos=16) == E                # max_start_pos + 1 > max_seq_len
+    assert _raw_decode_at(a, max_pos=-1) == E
+    assert _raw_decode_at(a, max_pos=15, freqs_end=15) == E  # RoPE table too short for the largest position
+    assert _raw_decode_at(a, pos=None) == E
+    assert _raw_decode_at(a, pos=(1 << 22) + 2) == E         # misaligned position pointer
+    assert _raw_decode_at(a, bsz=3) == E
+    assert _raw_decode_at(a, dtype=dba.LLAMA_F32) == U       # bf16 only
+    # the workspace for the largest position suffices
+    need = dba.llama_block_workspace_size(a, 1, 1, 15, dba.LLAMA_BF16)
+    assert _raw_decode_at(a, max_pos=15, ws_bytes=need - 1) == W

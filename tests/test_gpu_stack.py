@@ -136,3 +136,87 @@ def test_stack_top_p_sampled_generation(host_weights):
     assert np.mean(a[0] != greedy[0]) > 0.5        # flat synthetic logits: sampling rarely picks the argmax
     del stack
     torch.cuda.empty_cache()
+
+
+def _device_position_decode(stack, prompt, steps, temperature=0.0, top_p=0.95, uniforms=None):
+    """The device-position step run eagerly (no graph): ids and logits of every step."""
+    bsz, S = prompt.shape
+    dev = prompt.device
+    out = torch.empty(steps + 1, bsz, dtype=torch.int32, device=dev)
+    logits = torch.empty(bsz, stack.vocab, dtype=torch.float32, device=dev)
+    stack.forward(prompt, 0, logits, out[0])
+    if temperature > 0:
+        L.llama_sample_top_p(logits, out[0], bsz, stack.vocab, temperature, top_p, uniforms[0])
+    tok = out[0].clone()
+    pos = torch.full((1,), S, dtype=torch.int32, device=dev)
+    u = torch.empty(bsz, dtype=torch.float32, device=dev)
+    lg = []
+    for t in range(1, steps + 1):
+        if temperature > 0:
+            u.copy_(uniforms[t])
+        stack.decode_step_at(tok, pos, S + steps - 1, logits, temperature, top_p, u)
+        out[t].copy_(tok)
+        lg.append(logits.clone())
+    return out, lg
+
+
+@pytest.mark.parametrize("temperature", [0.0, 0.8])
+def test_stack_graph_decode_replays_match_eager(host_weights, temperature):
+    """generate(graph=True) captures one whole decode step (embedding, 32 layers,
+    norm, output projection, token choice, position advance) in a HIP graph and
+    replays it.  Every replay, with eager library work and a synchronisation
+    between replays, must reproduce the same step run eagerly through the same
+    device-position entry point bit for bit (ids and fp32 logits).  Against the
+    host-position path (llama_block_forward), whose attention splits follow the
+    actual length rather than the largest one, the logits agree to rounding and
+    the ids wherever the top two logits are not within rounding of each other."""
+    dev = need_gpu()
+    layers, emb, norm_w, w_out = host_weights
+    w = W5
+    steps, S = 10, 128
+    print(f"case {w.name}: HIP-graph decode, B={w.batch} prompt {S} + {steps} steps, T={temperature}", flush=True)
+    stack = StackRunner(model_args_for(w), lambda l: layers[l], emb, norm_w, w_out, torch.bfloat16, dev)
+    prompt = wl.prompt_tokens(w)[:, :S].contiguous().to(dev)
+    g = torch.Generator(device=dev).manual_seed(123)
+    uni = torch.rand(steps + 1, w.batch, generator=g, device=dev)
+    kw = dict(temperature=temperature, top_p=0.95, uniforms=uni) if temperature > 0 else {}
+    scratch_x = torch.randn(w.batch, w.dim, generator=g, device=dev).to(torch.bfloat16)
+    scratch_y = torch.empty_like(scratch_x)
+    graph_logits = {}
+
+    def on_step(t, logits, nxt):
+        if t == 0:
+            return
+        graph_logits[t] = logits.clone()
+        torch.cuda.synchronize()
+        # eager library work between replays
+        L.llama_rmsnorm(scratch_x, stack.norm_w, scratch_y, w.batch, w.dim, w.norm_eps)
+        torch.cuda.synchronize()
+
+    got = stack.generate(prompt, steps, on_step, graph=True, **kw)
+    torch.cuda.synchronize()
+    ref, ref_logits = _device_position_decode(stack, prompt, steps, **kw)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.cpu().numpy(), ref.cpu().numpy())
+    for t in range(1, steps + 1):
+        assert torch.equal(graph_logits[t], ref_logits[t - 1]), f"step {t}: replay differs from the eager step"
+    # host-position path
+    host_logits = {}
+    host = stack.generate(prompt, steps, lambda t, lg, n: host_logits.__setitem__(t, lg.clone()), **kw)
+    torch.cuda.synchronize()
+    hid, gid = host.cpu().numpy(), got.cpu().numpy()
+    np.testing.assert_array_equal(hid[0], gid[0])     # the same prefill call
+    for t in range(1, steps + 1):
+        # rows whose ids so far agree have identical inputs: their logits agree to rounding
+        same = np.all(hid[:t] == gid[:t], axis=0)
+        a, b = f64(host_logits[t])[same], f64(graph_logits[t])[same]
+        scale = np.abs(a).max()
+        assert np.abs(a - b).max() <= 1e-3 * scale, f"step {t}"
+        if temperature == 0:
+            top2 = np.sort(a, axis=1)[:, -2:]
+            clear = (top2[:, 1] - top2[:, 0]) > 1e-3 * scale
+            np.testing.assert_array_equal(hid[t][same][clear], gid[t][same][clear])
+    assert np.mean(np.all(hid == gid, axis=0)) >= 0.9   # a near tie may fork a row, rarely
+    print(f"[graph] {steps} replays bit-identical to the eager device-position steps", flush=True)
+    del stack
+    torch.cuda.empty_cache()

@@ -176,3 +176,41 @@ def test_determinism_batch_independence_causality():
     torch.cuda.synchronize()
     assert torch.equal(o3[:, :t], o1[:, :t]), "an output before the perturbed position changed"
     assert not torch.equal(o3[:, t], o1[:, t])
+
+
+def test_decode_at_device_position_matches_oracle():
+    """llama_block_decode_at reads the position from device memory.  With a bound
+    far above the actual position (max_start_pos 4000 while the steps run at
+    100..105) the attention splits are laid out for 4001 keys and all but the
+    first are empty; the outputs and the appended cache rows must still follow
+    the oracle's prefill + decode chain."""
+    from decoder_block_amd import _lib as L
+    dev = need_gpu()
+    w = SMALL
+    a, max_pos = w.prefill_len, 4000
+    print(f"case {w.name}: device-position decode at {a}..{a + w.decode_steps - 1}, bound {max_pos}", flush=True)
+    args = model_args_for(w, max_seq=max_pos + 1)
+    r = BlockRunner(args, wl.block_weights(w), torch.bfloat16, dev)
+    x = wl.activations(w).to(dev)
+    parts = [r.forward(x[:, :a].contiguous(), 0)]
+    need = L.llama_block_workspace_size(args, w.batch, 1, max_pos, L.LLAMA_BF16)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    pos = torch.empty(1, dtype=torch.int32, device=dev)
+    for t in range(w.decode_steps):
+        pos.fill_(a + t)
+        xt = x[:, a + t:a + t + 1].contiguous()
+        out = torch.empty_like(xt)
+        L.llama_block_decode_at(args, r.cw, r.cache_k, r.cache_v, r.freqs, r.freqs_end, xt, out, w.batch, pos,
+                                max_pos, ws, need)
+        parts.append(out)
+    torch.cuda.synchronize()
+    chain = torch.cat(parts, dim=1)
+    shape = (w.batch, w.max_seq_len, w.n_kv_heads, w.head_dim)
+    ck, cv = np.zeros(shape), np.zeros(shape)
+    n = a + w.decode_steps
+    ref = ob.block_forward(f64(x[:, :n]), _w64(wl.block_weights(w)), ck, cv, 0, w.n_heads, w.n_kv_heads,
+                           w.norm_eps, w.rope_theta)
+    check(chain, ref, "bf16", "prefill + device-position decode chain")
+    check(r.cache_k[:, :n], ck[:, :n], "bf16", "cache_k rows")
+    check(r.cache_v[:, :n], cv[:, :n], "bf16", "cache_v rows")
+    assert not torch.any(r.cache_k[:, n:]), "rows past the last position must stay untouched"
