@@ -14,6 +14,22 @@ import torch
 from . import _lib as L
 
 
+def check_weight_shapes(args: L.ModelArgs, weights: Dict[str, torch.Tensor]) -> None:
+    """The C ABI receives bare pointers and derives every extent from ``args`` (the
+    FFN width from dim, multiple_of and ffn_dim_multiplier): weights of another shape
+    would be read out of bounds, so their shapes are checked here, on the host."""
+    D, H = args.dim, args.n_heads
+    Hkv = args.n_kv_heads or H
+    d = D // H
+    F = L.llama_ffn_hidden_dim(args)
+    want = {"attention_norm": (D,), "ffn_norm": (D,), "wq": (H * d, D), "wk": (Hkv * d, D), "wv": (Hkv * d, D),
+            "wo": (D, H * d), "w1": (F, D), "w3": (F, D), "w2": (D, F)}
+    for name, shape in want.items():
+        got = tuple(weights[name].shape)
+        if got != shape:
+            raise ValueError(f"weight {name} has shape {got}; the model arguments imply {shape}")
+
+
 class BlockRunner:
     def __init__(self, args: L.ModelArgs, weights: Dict[str, torch.Tensor], dtype: torch.dtype,
                  device="cuda:0", cache=None, share_freqs=None):
@@ -23,6 +39,7 @@ class BlockRunner:
         self.device = torch.device(device)
         self.head_dim = args.dim // args.n_heads
         n_kv = args.n_kv_heads or args.n_heads
+        check_weight_shapes(args, weights)
         self.w = {k: v.to(self.device, dtype) for k, v in weights.items()}
         self.cw = L.block_weights(self.w)
         if cache is None:

@@ -181,3 +181,16 @@ def test_block_decode_at_validation_errors():
     # the workspace for the largest position suffices
     need = dba.llama_block_workspace_size(a, 1, 1, 15, dba.LLAMA_BF16)
     assert _raw_decode_at(a, max_pos=15, ws_bytes=need - 1) == W
+
+
+def test_runner_rejects_weights_of_another_shape():
+    """The C ABI derives every extent from the model arguments (the FFN width from
+    dim, multiple_of and ffn_dim_multiplier); the Python runner checks the weight
+    shapes against them before anything reaches the device."""
+    from decoder_block_amd.runner import check_weight_shapes, model_args_for
+    w = wl.Workload(31, "ffn-width-mismatch", "bf16", 2048, 16, 8, 1024, 256, None, 1e-5, 5e5, batch=1,
+                    prefill_len=4, decode_steps=0)
+    with pytest.raises(ValueError, match="w1"):
+        check_weight_shapes(model_args_for(w), wl.block_weights(w))
+    ok = w.scaled(ffn_hidden=1536, ffn_dim_multiplier=0.25)
+    check_weight_shapes(model_args_for(ok), wl.block_weights(ok))

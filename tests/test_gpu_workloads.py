@@ -128,23 +128,26 @@ def test_llama2_70b_block_decode_batch32():
 # ----------------------------------------------------------------------------- invariants
 SMALL = wl.Workload(30, "small-gqa", "bf16", 512, 8, 2, 1536, 256, None, 1e-5, 1e4, batch=3, prefill_len=100,
                     decode_steps=6)
+# 8 kv heads of head_dim 128: decode attention takes its one-workgroup-per-row layout
+SMALL_ROWS = wl.Workload(31, "small-gqa-8kv", "bf16", 2048, 16, 8, 1536, 256, 0.25, 1e-5, 5e5, batch=3,
+                         prefill_len=100, decode_steps=6)
 
 
-def _small_runner(dev, batch=None):
-    w = SMALL
+def _small_runner(dev, batch=None, w=SMALL):
     return BlockRunner(model_args_for(w, max_batch=batch or w.batch), wl.block_weights(w), torch.bfloat16, dev)
 
 
-def test_decode_chain_matches_prefill_and_oracle():
+@pytest.mark.parametrize("w", [SMALL, SMALL_ROWS], ids=lambda w: w.name)
+def test_decode_chain_matches_prefill_and_oracle(w):
     dev = need_gpu()
-    w = SMALL
+    print(f"case {w.name}: prefill + decode chain + chunked prefill", flush=True)
     x = wl.activations(w).to(dev)
     a = w.prefill_len
-    full = _small_runner(dev).forward(x, 0)
-    r = _small_runner(dev)
+    full = _small_runner(dev, w=w).forward(x, 0)
+    r = _small_runner(dev, w=w)
     parts = [r.forward(x[:, :a].contiguous(), 0)]
     parts += [r.forward(x[:, a + t:a + t + 1].contiguous(), a + t) for t in range(w.decode_steps)]
-    chunk = _small_runner(dev)
+    chunk = _small_runner(dev, w=w)
     c = [chunk.forward(x[:, :40].contiguous(), 0), chunk.forward(x[:, 40:].contiguous(), 40)]
     torch.cuda.synchronize()
     chain = torch.cat(parts, dim=1)
@@ -178,16 +181,17 @@ def test_determinism_batch_independence_causality():
     assert not torch.equal(o3[:, t], o1[:, t])
 
 
-def test_decode_at_device_position_matches_oracle():
+@pytest.mark.parametrize("max_pos", [4000, 137])
+@pytest.mark.parametrize("w", [SMALL, SMALL_ROWS], ids=lambda w: w.name)
+def test_decode_at_device_position_matches_oracle(w, max_pos):
     """llama_block_decode_at reads the position from device memory.  With a bound
-    far above the actual position (max_start_pos 4000 while the steps run at
-    100..105) the attention splits are laid out for 4001 keys and all but the
-    first are empty; the outputs and the appended cache rows must still follow
-    the oracle's prefill + decode chain."""
+    above the actual position (max_start_pos 4000 or 137 while the steps run at
+    100..105) the attention splits are laid out for the bound's length, and the
+    later ones are empty; the outputs and the appended cache rows must still
+    follow the oracle's prefill + decode chain."""
     from decoder_block_amd import _lib as L
     dev = need_gpu()
-    w = SMALL
-    a, max_pos = w.prefill_len, 4000
+    a = w.prefill_len
     print(f"case {w.name}: device-position decode at {a}..{a + w.decode_steps - 1}, bound {max_pos}", flush=True)
     args = model_args_for(w, max_seq=max_pos + 1)
     r = BlockRunner(args, wl.block_weights(w), torch.bfloat16, dev)
