@@ -181,6 +181,20 @@ def cpu_baseline(w, wts, x):
             "sample": f"the whole {w.name} workload ({B} x {S}-token prefill), numpy float64, {dt:.1f} s"}
 
 
+def cpu_decode_step_us(w, wts, x, cache_k, cache_v, p0):
+    """The oracle (numpy float64) on one one-token call of a decode workload: microseconds."""
+    import numpy as np
+    import torch
+    from oracle import block as ob
+    W = {k: v.to(torch.float64).numpy() for k, v in wts.items()}
+    ck = np.array(cache_k, dtype=np.float64)
+    cv = np.array(cache_v, dtype=np.float64)
+    xs = x.to(torch.float64).numpy()
+    t0 = time.perf_counter()
+    ob.block_forward(xs, W, ck, cv, p0, w.n_heads, w.n_kv_heads, w.norm_eps, w.rope_theta)
+    return (time.perf_counter() - t0) * 1e6
+
+
 def bench_stack(dev, steps):
     """32 layers + embedding + LM head: prefill of 64 x 2048 prompts, then greedy one-token steps."""
     import torch
@@ -371,6 +385,18 @@ def main():
                 "stage_us": {n: round(v * 1e3, 2) for n, v in zip(STAGES, st4)}}
         del r4, flush
         torch.cuda.empty_cache()
+        if not a.no_cpu_baseline:
+            import numpy as np
+            log("cpu oracle: one decode step of each decode workload")
+            c4k, c4v = (c.to(torch.float32).numpy() for c in cache)
+            dec4["cpu_oracle_step_us"] = round(cpu_decode_step_us(w4, wts4, wl.activations(w4), c4k, c4v, p0), 1)
+            dec4["cpu_oracle_note"] = "oracle, numpy float64, one call over the same seeded cache (host cores)"
+            shape3 = (1, S3 + 1, w3.n_kv_heads, w3.head_dim)
+            x3d = wl.activations(w3)[:, S3:S3 + 1].contiguous()
+            dec3["cpu_oracle_step_us"] = round(cpu_decode_step_us(w3, wts3, x3d, np.zeros(shape3), np.zeros(shape3),
+                                                                  S3), 1)
+            dec3["cpu_oracle_note"] = ("oracle, numpy float64, one call at position 8192 over a zero cache of the "
+                                       "same shape (its cost depends on the shape only)")
         extra.update({"llama3_8b_prefill_8192": pre3, "llama3_8b_decode": dec3, "llama2_70b_decode_b32": dec4})
 
     if a.stack:
