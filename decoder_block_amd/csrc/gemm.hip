@@ -627,8 +627,9 @@ hipError_t launch_bf16(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, in
     }
     return launch_dma<64, 128, kSkinnyBK, 2, 6, DUAL, 4>(A, lda, w, M, N, K, epi, splits, partial, st);
   }
-  if (lda % 8 == 0 && M > 64 && K % kBigBK == 0 && splits <= 1)
-    return launch_dma<256, 256, kBigBK, 2, kBigStages, DUAL, kBigWaves>(A, lda, w, M, N, K, epi, 1, partial, st);
+  if (lda % 8 == 0 && M > 64 && K % kBigBK == 0)
+    return launch_dma<256, 256, kBigBK, 2, kBigStages, DUAL, kBigWaves>(A, lda, w, M, N, K, epi, splits, partial,
+                                                                        st);
   hipError_t e;
   if (M <= 32) {
     if constexpr (DUAL)
@@ -663,7 +664,19 @@ hipError_t launch_f32(const float* A, int64_t lda, WeightRows<float> w, int M, i
 }  // namespace
 
 int gemm_pick_splits(int M, int N, int K, bool dual, bool is_bf16) {
-  if (M > 64) return 1;
+  if (M > 64) {
+    // 256 x 256 tiles: split K only when the tiles would leave at least half the
+    // CUs idle (a 2048-token chunk's wo and w2 make 128 tiles), each split keeping
+    // at least 8 k-tiles of pipeline; otherwise one pass over K
+    if (!is_bf16 || K % kBigBK != 0) return 1;
+    const int tiles = ((M + 255) / 256) * ((N + (dual ? 127 : 255)) / (dual ? 128 : 256));
+    if (tiles > kCUs / 2) return 1;
+    const int nkt = K / kBigBK;
+    const int s = min(kCUs / tiles, nkt / 8);
+    if (s <= 1) return 1;
+    const int per = (nkt + s - 1) / s;
+    return (nkt + per - 1) / per;
+  }
   // small token count: the weights stream from HBM once; split K so that the
   // grid covers the CUs
   if (is_bf16 && K % kSkinnyBK == 0) {
