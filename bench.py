@@ -124,18 +124,30 @@ def flush_mall(buf):
 
 
 def time_decode(r, xs, p0s, flush):
-    """Times each one-token call separately with events (MALL flushed before each)."""
+    """Times each one-token call separately (MALL flushed before each): the step
+    between two events around the call, then the stages in a second pass with an
+    event after each stage (each event adds a few microseconds of its own, so
+    the stages are not summed into the step time).  Repeating a call at the same
+    position rewrites the same cache row with the same values."""
     import torch
     bsz = xs[0].shape[0]
     r.reserve(bsz, 1, max(p0s))
     out = torch.empty_like(xs[0])
+    r.forward(xs[0], p0s[0], out)          # untimed: loads the kernels' code on first use
+    torch.cuda.synchronize()
     tot, stage_tot = [], [0.0] * 7
     for x, p0 in zip(xs, p0s):
+        flush_mall(flush)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        r.forward(x, p0, out)
+        e1.record()
+        torch.cuda.synchronize()
+        tot.append(e0.elapsed_time(e1))
         flush_mall(flush)
         e = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
         r.forward(x, p0, out, events=e)
         torch.cuda.synchronize()
-        tot.append(e[0].elapsed_time(e[7]))
         for i in range(1, 8):
             stage_tot[i - 1] += e[i - 1].elapsed_time(e[i])
     n = len(xs)

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libllama_block.so")
-SOURCES = ["api.hip", "gemm.hip", "attention.hip", "misc.hip", "sample.hip"]
+SOURCES = ["api.hip", "gemm.hip", "gemv.hip", "attention.hip", "misc.hip", "sample.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -137,17 +137,28 @@ int block_forward_t(const Dims& g, const llama_model_args* a, const llama_block_
   const bool bf = sizeof(T) == 2;
   const llama_dtype dt = bf ? LLAMA_BF16 : LLAMA_F32;
   const int nq = g.H * g.d, nkv = g.Hkv * g.d;
-  hipError_t e;
+  hipError_t e = hipSuccess;
   // h = x + wo(attention(RMSNorm(x))).  RMSNorm(x) W^T is computed as
   // rsqrt(mean(x^2) + eps) * ((x * g) W^T): the row factor is applied to the fp32
   // accumulators, so the normalised activation is never rounded to bf16.
-  e = llama::rmsnorm<T>(x, g.D, (const T*)w->attention_norm, xn, M, g.D, a->norm_eps, st, r1);
+  // Up to four tokens in bf16: the weight-streaming kernels take the un-normalised
+  // rows and apply the same factor themselves, so no normalisation pass runs.
+  const bool fused_norm = bf && llama::gemv_fits(M, nq + 2 * nkv, g.D, g.D) && llama::gemv_fits(M, g.F, g.D, g.D);
+  if (!fused_norm) e = llama::rmsnorm<T>(x, g.D, (const T*)w->attention_norm, xn, M, g.D, a->norm_eps, st, r1);
   if (e != hipSuccess || mark(1) != hipSuccess) return LLAMA_ERR_HIP;
   {
     llama::WeightRows<T> wr{(const T*)w->wq, (const T*)w->wk, (const T*)w->wv, nq, nq + nkv};
-    llama::EpiQKV<T> epi{q, ck, cv, freqs, seqlen, start_pos, a->max_seq_len, nq, nkv, g.d, r1, pos_dev};
     const int N = nq + 2 * nkv;
-    e = llama::gemm_launch<T>(xn, g.D, wr, M, N, g.D, epi, llama::gemm_pick_splits(M, N, g.D, false, bf), part, st);
+    if constexpr (sizeof(T) == 2) {
+      if (fused_norm) {
+        llama::EpiQKV<T> epi{q, ck, cv, freqs, seqlen, start_pos, a->max_seq_len, nq, nkv, g.d, nullptr, pos_dev};
+        e = llama::gemv_launch(x, g.D, wr, M, N, g.D, (const T*)w->attention_norm, a->norm_eps, epi, st);
+      }
+    }
+    if (!fused_norm) {
+      llama::EpiQKV<T> epi{q, ck, cv, freqs, seqlen, start_pos, a->max_seq_len, nq, nkv, g.d, r1, pos_dev};
+      e = llama::gemm_launch<T>(xn, g.D, wr, M, N, g.D, epi, llama::gemm_pick_splits(M, N, g.D, false, bf), part, st);
+    }
     if (e != hipSuccess || mark(2) != hipSuccess) return LLAMA_ERR_HIP;
   }
   llama::AttnShape sh{bsz, seqlen, start_pos, g.H, g.Hkv, g.d, a->max_seq_len};
@@ -163,12 +174,21 @@ int block_forward_t(const Dims& g, const llama_model_args* a, const llama_block_
     if (e != hipSuccess || mark(4) != hipSuccess) return LLAMA_ERR_HIP;
   }
   // out = h + w2(silu(w1 hn) * w3 hn), hn = RMSNorm(h)
-  e = llama::rmsnorm<T>(h, g.D, (const T*)w->ffn_norm, hn, M, g.D, a->norm_eps, st, r2);
+  if (!fused_norm) e = llama::rmsnorm<T>(h, g.D, (const T*)w->ffn_norm, hn, M, g.D, a->norm_eps, st, r2);
   if (e != hipSuccess || mark(5) != hipSuccess) return LLAMA_ERR_HIP;
   {
-    llama::EpiSwiGLU<T> epi{gt, g.F, r2};
-    e = llama::gemm_dual_launch<T>(hn, g.D, (const T*)w->w1, (const T*)w->w3, M, g.F, g.D, epi,
-                                   llama::gemm_pick_splits(M, g.F, g.D, true, bf), part, st);
+    if constexpr (sizeof(T) == 2) {
+      if (fused_norm) {
+        llama::EpiSwiGLU<T> epi{gt, g.F, nullptr};
+        e = llama::gemv_dual_launch(h, g.D, (const T*)w->w1, (const T*)w->w3, M, g.F, g.D, (const T*)w->ffn_norm,
+                                    a->norm_eps, epi, st);
+      }
+    }
+    if (!fused_norm) {
+      llama::EpiSwiGLU<T> epi{gt, g.F, r2};
+      e = llama::gemm_dual_launch<T>(hn, g.D, (const T*)w->w1, (const T*)w->w3, M, g.F, g.D, epi,
+                                     llama::gemm_pick_splits(M, g.F, g.D, true, bf), part, st);
+    }
     if (e != hipSuccess || mark(6) != hipSuccess) return LLAMA_ERR_HIP;
   }
   {

@@ -37,6 +37,9 @@ namespace llama {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+// decode workgroups resident at once: 4 waves each, 2 waves per SIMD (the
+// kernel's register budget), 4 SIMDs per CU, 256 CUs
+constexpr int kResidentDecodeWgs = 2 * 256;
 
 // ------------------------------------------------------------------ KV append
 template <typename T>
@@ -379,13 +382,13 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
       const int key = min(c0 + kt * 16 + l16, t_end - 1);
 #pragma unroll
       for (int kk = 0; kk < HD / 32; ++kk)
-        kf[kt][kk] = *(const bf16x8*)(kbase + (uint32_t)(key * rstride + (kk * 4 + g) * 8));
+        kf[kt][kk] = load_stream8(kbase + (uint32_t)(key * rstride + (kk * 4 + g) * 8));
     }
     if (vtask) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int key = min(c0 + (e < 4 ? vg * 4 + e : 16 + vg * 4 + (e - 4)), t_end - 1);
-        vk[e] = *(const bf16x8*)(vbase + (uint32_t)(key * rstride + vdc * 8));
+        vk[e] = load_stream8(vbase + (uint32_t)(key * rstride + vdc * 8));
       }
     }
   };
@@ -524,52 +527,74 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
   }
 }
 
-// Log-sum-exp merge of the split partials of one (b, head): 256 threads, the
-// splits spread over the threads (no serial walk over the splits).
-template <typename T>
+// Log-sum-exp merge of the split partials of one (b, head).  Wave w takes the
+// splits w, w + 4, ...; each lane owns HD / 64 output dimensions.  A wave loads
+// up to 16 splits (maximum, sum and its dimensions of o) before using any of
+// them, keeps a running (max, sum, o) that it rescales as the maximum grows,
+// and the four waves merge in LDS: one memory round trip for up to 64 splits.
+// Maxima are in the log2 domain of the decode kernel; an empty split (max -inf)
+// weighs 0, and split 0 always holds keys, so the total sum is positive.
+template <typename T, int HD>
 __global__ void __launch_bounds__(256)
-attn_decode_combine(const float* __restrict__ partial, T* __restrict__ out, int nsplit, int HD) {
-  __shared__ float red[256];
-  __shared__ float wz[1024];
+attn_decode_combine(const float* __restrict__ partial, T* __restrict__ out, int nsplit) {
+  constexpr int PD = HD / 64;
+  constexpr int NB = 16;
+  __shared__ float sm[4], sl[4], so[4][HD];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t bh = blockIdx.x;
-  const int t = threadIdx.x;
   const float* base = partial + bh * nsplit * (HD + 2);
-  // 1) global max of the split maxima
-  float M = -INFINITY;
-  for (int z = t; z < nsplit; z += 256) M = fmaxf(M, base[z * (HD + 2) + HD]);
-  M = wave_max(M);
-  if ((t & 63) == 0) red[t >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  // 2) split weights and the total sum
-  float Ls = 0.f;
-  for (int z = t; z < nsplit; z += 256) {
-    const float* p = base + z * (HD + 2);
-    const float w = p[HD] == -INFINITY ? 0.f : exp2f(p[HD] - M);
-    if (z < 1024) wz[z] = w;
-    Ls += w * p[HD + 1];
+  float M = -INFINITY, Ls = 0.f, o[PD];
+#pragma unroll
+  for (int k = 0; k < PD; ++k) o[k] = 0.f;
+  for (int z0 = wave; z0 < nsplit; z0 += 4 * NB) {
+    float mz[NB], lz[NB], oz[NB][PD];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int z = z0 + 4 * i;
+      const float* p = base + (int64_t)min(z, nsplit - 1) * (HD + 2);
+      mz[i] = z < nsplit ? p[HD] : -INFINITY;
+      lz[i] = p[HD + 1];
+#pragma unroll
+      for (int k = 0; k < PD; ++k) oz[i][k] = p[lane * PD + k];
+    }
+    float mb = M;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) mb = fmaxf(mb, mz[i]);
+    if (mb == -INFINITY) continue;
+    const float a = exp2f(M - mb);
+    Ls *= a;
+#pragma unroll
+    for (int k = 0; k < PD; ++k) o[k] *= a;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const float w = exp2f(mz[i] - mb);
+      Ls += w * lz[i];
+#pragma unroll
+      for (int k = 0; k < PD; ++k) o[k] += w * oz[i][k];
+    }
+    M = mb;
   }
-  Ls = wave_sum(Ls);
-  if ((t & 63) == 0) red[t >> 6] = Ls;
-  __syncthreads();
-  Ls = red[0] + red[1] + red[2] + red[3];
-  // 3) weighted sum of the partial outputs: thread (d, zs) sums splits zs, zs+R, ...
-  const int R = 256 / HD;
-  const int d = t % HD, zs = t / HD;
-  float acc = 0.f;
-#pragma unroll 8
-  for (int z = zs; z < nsplit; z += R) {
-    const float* p = base + z * (HD + 2);
-    const float w = z < 1024 ? wz[z] : (p[HD] == -INFINITY ? 0.f : exp2f(p[HD] - M));
-    acc += w * p[d];
+  if (lane == 0) {
+    sm[wave] = M;
+    sl[wave] = Ls;
   }
+#pragma unroll
+  for (int k = 0; k < PD; ++k) so[wave][lane * PD + k] = o[k];
   __syncthreads();
-  red[t] = acc;
-  __syncthreads();
-  if (zs == 0) {
-    for (int r = 1; r < R; ++r) acc += red[r * HD + d];
-    out[bh * HD + d] = from_f<T>(acc / Ls);
+  if (wave != 0) return;
+  const float Mx = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+  float wt[4], tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    wt[w] = sm[w] == -INFINITY ? 0.f : exp2f(sm[w] - Mx);
+    tot += wt[w] * sl[w];
+  }
+  const float inv = 1.0f / tot;
+#pragma unroll
+  for (int k = 0; k < PD; ++k) {
+    const int d = lane * PD + k;
+    const float acc = wt[0] * so[0][d] + wt[1] * so[1][d] + wt[2] * so[2][d] + wt[3] * so[3][d];
+    out[bh * HD + d] = from_f<T>(acc * inv);
   }
 }
 
@@ -615,7 +640,12 @@ hipError_t attn_prefill(const T* q, const T* cache_k, const T* cache_v, T* out, 
 int attn_decode_splits(int bsz, int n_heads, int n_kv_heads, int T) {
   const int n_rep = n_heads / n_kv_heads;
   const int units = bsz * n_kv_heads * ((n_rep + 15) / 16);
+  // two rounds of the 512 workgroups that are resident at once (two per CU);
+  // when that leaves under 1024 keys per split, the whole grid is one round
+  // instead: a split is then a single latency-bound pass, and a second round
+  // would double the kernel's time
   int ns = (1024 + units - 1) / units;
+  if ((T + ns - 1) / ns < 1024) ns = max(1, kResidentDecodeWgs / units);
   ns = max(1, min(ns, (T + 127) / 128));
   int L = (T + ns - 1) / ns;
   L = (L + 31) / 32 * 32;
@@ -641,7 +671,10 @@ hipError_t attn_decode(const T* q, const T* cache_k, const T* cache_v, T* out, c
                                                  pos_dev);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1) return e;
-    attn_decode_combine<T><<<sh.bsz * sh.n_heads, 256, 0, st>>>(partial, out, ns, sh.head_dim);
+    if (sh.head_dim == 128)
+      attn_decode_combine<T, 128><<<sh.bsz * sh.n_heads, 256, 0, st>>>(partial, out, ns);
+    else
+      attn_decode_combine<T, 64><<<sh.bsz * sh.n_heads, 256, 0, st>>>(partial, out, ns);
   } else {
     if (pos_dev) return hipErrorNotSupported;
     const int64_t waves = (int64_t)sh.bsz * sh.n_heads;

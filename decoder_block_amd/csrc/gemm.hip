@@ -31,6 +31,8 @@ constexpr int kCUs = 256;         // MI355X compute units
 // 6 stages.  Narrow tiles need fewer K-splits to cover the CUs (measured:
 // LLaMA-3-8B-shaped w1/w3 at M = 64 went from 70 to 48 us).
 constexpr int kSkinnyBK = 64;
+// cache-policy operand of the LDS-DMA load: the non-temporal bit (gfx940 family)
+constexpr int kCpolNT = 2;
 
 template <typename T>
 __device__ __forceinline__ const T* weight_row(const WeightRows<T>& w, int n, int K) {
@@ -279,11 +281,19 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
   // bank-group swizzle of the 16-byte chunks: a ds_read_b128 phase reads one
   // chunk of 16 consecutive rows, which must hit 16 distinct bank groups
   auto swz = [](int r) { return BK == 32 ? ((r >> 2) & 3) : ((r >> 1) & 7); };
+  // Small-M tiles read every weight element exactly once: their weight blocks
+  // carry the non-temporal hint.  The hint is an immediate of the instruction,
+  // so there the blocks are dealt i-major (block i * NW + wave): the first
+  // A_LOADS loads of every wave are activation rows, the rest weight rows.
+  constexpr bool kStreamW = BM <= 64;
+  constexpr int A_LOADS = kStreamW ? (BM / RPB) / NW : 0;
+  static_assert(!kStreamW || (BM / RPB) % NW == 0, "activation rows must fill whole load slots");
+  auto blk_of = [&](int i) { return kStreamW ? i * NW + wave : wave * LOADS + i; };
   // this lane's source row pointer (+ chunk offset) for each of its DMA blocks
   const bf16* src[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int blk = wave * LOADS + i;
+    const int blk = blk_of(i);
     const int r = blk * RPB + lane / CH;
     const int c = (lane % CH) ^ swz(r);
     const bf16* p;
@@ -306,9 +316,14 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
     const int st = kt % NS;
     const int kc = min(kt, nk - 1);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      LLAMA_LDS void* dst = (LLAMA_LDS void*)&smem[st][(wave * LOADS + i) * 64];
+    for (int i = 0; i < A_LOADS; ++i) {
+      LLAMA_LDS void* dst = (LLAMA_LDS void*)&smem[st][blk_of(i) * 64];
       __builtin_amdgcn_global_load_lds((const void*)(src[i] + kc * BK), dst, 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = A_LOADS; i < LOADS; ++i) {
+      LLAMA_LDS void* dst = (LLAMA_LDS void*)&smem[st][blk_of(i) * 64];
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + kc * BK), dst, 16, 0, kStreamW ? kCpolNT : 0);
     }
   };
   auto wrow = [&](int t) {
@@ -677,6 +692,9 @@ int gemm_pick_splits(int M, int N, int K, bool dual, bool is_bf16) {
     const int per = (nkt + s - 1) / s;
     return (nkt + per - 1) / per;
   }
+  // up to four tokens: the weight-streaming kernel, one pass over K
+  // (gemm_launch sends the problem there when its shapes allow)
+  if (is_bf16 && gemv_fits(M, N, K, K)) return 1;
   // small token count: the weights stream from HBM once; split K so that the
   // grid covers the CUs
   if (is_bf16 && K % kSkinnyBK == 0) {
@@ -713,9 +731,11 @@ template <typename T, class Epi>
 hipError_t gemm_launch(const T* A, int64_t lda, WeightRows<T> w, int M, int N, int K, Epi epi,
                        int splits, float* partial, hipStream_t st) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  if constexpr (sizeof(T) == 2)
+  if constexpr (sizeof(T) == 2) {
+    if (gemv_fits(M, N, K, lda) && w.n1 % 4 == 0 && w.n2 % 4 == 0)
+      return gemv_launch<Epi>(A, lda, w, M, N, K, nullptr, 0.0f, epi, st);
     return launch_bf16<false>(A, lda, w, M, N, K, epi, splits, partial, st);
-  else
+  } else
     return launch_f32<false>(A, lda, w, M, N, K, epi, splits, partial, st);
 }
 
@@ -724,9 +744,10 @@ hipError_t gemm_dual_launch(const T* A, int64_t lda, const T* w1, const T* w3, i
                             Epi epi, int splits, float* partial, hipStream_t st) {
   if (M <= 0 || N <= 0) return hipSuccess;
   WeightRows<T> w{w1, w3, nullptr, N, N};
-  if constexpr (sizeof(T) == 2)
+  if constexpr (sizeof(T) == 2) {
+    if (gemv_fits(M, N, K, lda)) return gemv_dual_launch<Epi>(A, lda, w1, w3, M, N, K, nullptr, 0.0f, epi, st);
     return launch_bf16<true>(A, lda, w, M, N, K, epi, splits, partial, st);
-  else
+  } else
     return launch_f32<true>(A, lda, w, M, N, K, epi, splits, partial, st);
 }
 

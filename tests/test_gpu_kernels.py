@@ -92,6 +92,11 @@ def test_rope_apply(dtype):
     ("bf16", 200, 1000, 260),     # large tiles, K not a multiple of 32 (register-staged kernel)
     ("bf16", 257, 64, 256),       # a single k-tile pair, one row past a tile
     ("bf16", 1024, 4096, 1536),   # several full 256x256 tiles
+    ("bf16", 1, 4096, 6144),      # one token: weight-streaming kernel, whole 512-wide chunks
+    ("bf16", 2, 1000, 260),       # K = 512 + 488: the last chunk is ragged
+    ("bf16", 4, 14336, 512),      # four tokens, 28 chunks (two in flight per wave, one left over)
+    ("bf16", 3, 40, 100),         # K below one chunk: most lanes idle
+    ("bf16", 4, 8, 4),            # one lane of one wave holds all of K; a single workgroup
     ("f32", 70, 260, 132),
 ])
 def test_linear(dtype, M, K, N):
@@ -110,7 +115,10 @@ def test_linear(dtype, M, K, N):
     # small M with split K: w1/w3 in 4 splits; w2 (K = 2816 = 44 k-tiles) in 11 splits of 4
     ("bf16", 9, 1024, 2816),
     # small M, dim = 352 is not whole 64-wide k-tiles (register-staged kernel for w1/w3)
-    ("bf16", 7, 352, 1024)])
+    ("bf16", 7, 352, 1024),
+    # one to four tokens: weight-streaming kernels (dim = 512 is one chunk: three waves idle;
+    # 640 = 512 + 128 and 1712 = 3 * 512 + 176 end in ragged chunks)
+    ("bf16", 1, 512, 1536), ("bf16", 4, 640, 1712), ("bf16", 2, 4096, 14336)])
 def test_swiglu_ffn(dtype, rows, dim, hidden):
     need_gpu()
     print(f"case swiglu {dtype} rows={rows} dim={dim} hidden={hidden}", flush=True)
@@ -207,12 +215,13 @@ def test_attn_decode(dtype, B, p0, H, Hkv, d):
 
 
 # ----------------------------------------------------------------------------- config-5 pieces
-def test_embedding_and_lm_head_argmax():
+@pytest.mark.parametrize("B", [6, 2])   # 2 rows: the weight-streaming kernel computes the logits
+def test_embedding_and_lm_head_argmax(B):
     need_gpu()
-    print("case embedding + lm_head", flush=True)
-    V, D, B = 1000, 256, 6
+    print(f"case embedding + lm_head B={B}", flush=True)
+    V, D = 1000, 256
     table = rnd((V, D), 0.02)
-    tok = torch.tensor([0, 999, 5, 17, 5, 300], dtype=torch.int32)
+    tok = torch.tensor([0, 999, 5, 17, 5, 300][:B], dtype=torch.int32)
     out = torch.empty(B, D, dtype=torch.bfloat16, device="cuda:0")
     dba.llama_embedding(dev(tok), dev(table), out, B, D, V)
     torch.cuda.synchronize()
