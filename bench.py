@@ -123,6 +123,12 @@ def flush_mall(buf):
     buf.sum()
 
 
+def pct(v, q):
+    """The q-quantile of the samples v (nearest rank)."""
+    s = sorted(v)
+    return s[min(len(s) - 1, max(0, int(round(q * (len(s) - 1)))))]
+
+
 def time_decode(r, xs, p0s, flush):
     """Times each one-token call separately (MALL flushed before each): the step
     between two events around the call, then the stages in a second pass with an
@@ -364,6 +370,7 @@ def main():
         attn_gbs = kvb / (st[2] * 1e-3) / 1e9
         dec3 = {"step_us_mean": round(1e3 * sum(tot) / len(tot), 2),
                 "step_us_median": round(1e3 * sorted(tot)[len(tot) // 2], 2),
+                "step_us_p10": round(1e3 * pct(tot, 0.1), 2), "step_us_p90": round(1e3 * pct(tot, 0.9), 2),
                 "attention_us": round(st[2] * 1e3, 2), "attention_gbs": round(attn_gbs, 1),
                 "attention_hbm_frac": round(attn_gbs / PEAK_HBM_GBS, 4),
                 "step_gbs": round((wb + kvb) / (sum(tot) / len(tot) * 1e-3) / 1e9, 1),
@@ -390,6 +397,7 @@ def main():
         attn4 = kvb4 / (st4[2] * 1e-3) / 1e9
         dec4 = {"step_us_mean": round(1e3 * sum(tot4) / n4, 2),
                 "step_us_median": round(1e3 * sorted(tot4)[n4 // 2], 2),
+                "step_us_p10": round(1e3 * pct(tot4, 0.1), 2), "step_us_p90": round(1e3 * pct(tot4, 0.9), 2),
                 "attention_us": round(st4[2] * 1e3, 2), "attention_gbs": round(attn4, 1),
                 "attention_hbm_frac": round(attn4 / PEAK_HBM_GBS, 4),
                 "step_gbs": round((wb4 + kvb4) / (sum(tot4) / n4 * 1e-3) / 1e9, 1),

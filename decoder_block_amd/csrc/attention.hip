@@ -323,7 +323,10 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
                  float scale_log2, const int32_t* __restrict__ pos_dev) {
   constexpr int CH = HD / 8;
   static_assert(HD == 64 || HD == 128, "head_dim");
+  constexpr int RPI = 64 / CH;                // K rows per load instruction (whole rows)
+  constexpr int KL = 32 / RPI;                // K loads per lane per 32-key chunk
   __shared__ bf16x8 Vt[4][HD * 4];          // per wave: [d][4 chunks of 8 permuted keys]
+  __shared__ bf16x8 Kt[4][32 * CH];         // per wave: [key][chunk ^ ksw(key)]
   __shared__ float mrg_m[4][16], mrg_l[4][16];
 
   const int H = sh.n_heads, Hkv = sh.n_kv_heads;
@@ -375,14 +378,18 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
   // guard and the softmax masks those keys out, so their V rows get weight 0.
   // Offsets within one sequence's cache rows fit 32 bits (the host rejects
   // max_seq * n_kv_heads * head_dim >= 2^31).
+  // K is loaded whole rows per instruction (CH lanes per key: a head's row is
+  // one contiguous piece), which streams measurably faster from HBM than the
+  // MFMA operand layout (16 keys x 64 bytes per instruction); the rows go
+  // through a per-wave LDS tile into that layout.  The swizzle ksw keeps both
+  // the row writes and the 16-key operand reads free of bank conflicts.
+  auto ksw = [](int r) { return HD == 128 ? (r & 15) : ((r >> 1) & 7); };
   const int rstride = (int)stride;
-  auto load = [&](int c0, bf16x8 (&kf)[2][HD / 32], bf16x8 (&vk)[8]) {
+  auto load = [&](int c0, bf16x8 (&kr)[KL], bf16x8 (&vk)[8]) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int key = min(c0 + kt * 16 + l16, t_end - 1);
-#pragma unroll
-      for (int kk = 0; kk < HD / 32; ++kk)
-        kf[kt][kk] = load_stream8(kbase + (uint32_t)(key * rstride + (kk * 4 + g) * 8));
+    for (int e = 0; e < KL; ++e) {
+      const int key = min(c0 + e * RPI + lane / CH, t_end - 1);
+      kr[e] = load_stream8(kbase + (uint32_t)(key * rstride + (lane % CH) * 8));
     }
     if (vtask) {
 #pragma unroll
@@ -392,7 +399,12 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
       }
     }
   };
-  auto compute = [&](int c0, const bf16x8 (&kf)[2][HD / 32], const bf16x8 (&vk)[8]) {
+  auto compute = [&](int c0, const bf16x8 (&kr)[KL], const bf16x8 (&vk)[8]) {
+#pragma unroll
+    for (int e = 0; e < KL; ++e) {
+      const int r = e * RPI + lane / CH;
+      Kt[wave][r * CH + ((lane % CH) ^ ksw(r))] = kr[e];
+    }
     if (vtask) {
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
@@ -409,8 +421,11 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int kk = 0; kk < HD / 32; ++kk)
-        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt][kk], qf[kk], sacc[kt], 0, 0, 0);
+      for (int kk = 0; kk < HD / 32; ++kk) {
+        const int r = kt * 16 + l16, c = kk * 4 + g;
+        const bf16x8 kf = Kt[wave][r * CH + (c ^ ksw(r))];
+        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kk], sacc[kt], 0, 0, 0);
+      }
     float mloc = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -459,7 +474,7 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
 
   const int c_first = t_begin + wave * 32;
   const int nit = c_first < t_end ? (t_end - c_first + 127) / 128 : 0;
-  bf16x8 kA[2][HD / 32], vA[8], kB[2][HD / 32], vB[8];
+  bf16x8 kA[KL], vA[8], kB[KL], vB[8];
   if (nit > 0) load(c_first, kA, vA);
   int it = 0;
   // (the scheduling barriers keep each prefetch ahead of the compute that
@@ -525,6 +540,43 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
       p[HD + 1] = Ls;
     }
   }
+}
+
+// The same merge for at most NB splits: one wave per (b, head), four rows per
+// workgroup, every split loaded before any is used, no LDS.
+template <typename T, int HD, int NB>
+__global__ void __launch_bounds__(256)
+attn_decode_combine_wave(const float* __restrict__ partial, T* __restrict__ out, int nsplit, int rows) {
+  constexpr int PD = HD / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t bh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (bh >= rows) return;
+  const float* base = partial + bh * nsplit * (HD + 2);
+  float mz[NB], lz[NB], oz[NB][PD];
+#pragma unroll
+  for (int z = 0; z < NB; ++z) {
+    const float* p = base + (int64_t)min(z, nsplit - 1) * (HD + 2);
+    mz[z] = z < nsplit ? p[HD] : -INFINITY;
+    lz[z] = p[HD + 1];
+#pragma unroll
+    for (int k = 0; k < PD; ++k) oz[z][k] = p[lane * PD + k];
+  }
+  float M = mz[0];
+#pragma unroll
+  for (int z = 1; z < NB; ++z) M = fmaxf(M, mz[z]);
+  float Ls = 0.f, o[PD];
+#pragma unroll
+  for (int k = 0; k < PD; ++k) o[k] = 0.f;
+#pragma unroll
+  for (int z = 0; z < NB; ++z) {
+    const float w = exp2f(mz[z] - M);
+    Ls += w * lz[z];
+#pragma unroll
+    for (int k = 0; k < PD; ++k) o[k] += w * oz[z][k];
+  }
+  const float inv = 1.0f / Ls;
+#pragma unroll
+  for (int k = 0; k < PD; ++k) out[bh * HD + lane * PD + k] = from_f<T>(o[k] * inv);
 }
 
 // Log-sum-exp merge of the split partials of one (b, head).  Wave w takes the
@@ -641,11 +693,12 @@ int attn_decode_splits(int bsz, int n_heads, int n_kv_heads, int T) {
   const int n_rep = n_heads / n_kv_heads;
   const int units = bsz * n_kv_heads * ((n_rep + 15) / 16);
   // two rounds of the 512 workgroups that are resident at once (two per CU);
-  // when that leaves under 1024 keys per split, the whole grid is one round
-  // instead: a split is then a single latency-bound pass, and a second round
-  // would double the kernel's time
+  // when that leaves under 4096 keys per split, the whole grid is one round
+  // instead: a short split is a single latency-bound pass that a second round
+  // would double, and one round of longer splits also measured faster (70B
+  // shape, batch 32 at 4097 keys: 2 splits of 2049 keys against 4 of 1025)
   int ns = (1024 + units - 1) / units;
-  if ((T + ns - 1) / ns < 1024) ns = max(1, kResidentDecodeWgs / units);
+  if ((T + ns - 1) / ns < 4096) ns = max(1, kResidentDecodeWgs / units);
   ns = max(1, min(ns, (T + 127) / 128));
   int L = (T + ns - 1) / ns;
   L = (L + 31) / 32 * 32;
@@ -671,10 +724,23 @@ hipError_t attn_decode(const T* q, const T* cache_k, const T* cache_v, T* out, c
                                                  pos_dev);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1) return e;
-    if (sh.head_dim == 128)
-      attn_decode_combine<T, 128><<<sh.bsz * sh.n_heads, 256, 0, st>>>(partial, out, ns);
-    else
-      attn_decode_combine<T, 64><<<sh.bsz * sh.n_heads, 256, 0, st>>>(partial, out, ns);
+    const int rows = sh.bsz * sh.n_heads;
+    const int wgs = (rows + 3) / 4;
+    if (ns <= 4) {
+      if (sh.head_dim == 128)
+        attn_decode_combine_wave<T, 128, 4><<<wgs, 256, 0, st>>>(partial, out, ns, rows);
+      else
+        attn_decode_combine_wave<T, 64, 4><<<wgs, 256, 0, st>>>(partial, out, ns, rows);
+    } else if (ns <= 16) {
+      if (sh.head_dim == 128)
+        attn_decode_combine_wave<T, 128, 16><<<wgs, 256, 0, st>>>(partial, out, ns, rows);
+      else
+        attn_decode_combine_wave<T, 64, 16><<<wgs, 256, 0, st>>>(partial, out, ns, rows);
+    } else if (sh.head_dim == 128) {
+      attn_decode_combine<T, 128><<<rows, 256, 0, st>>>(partial, out, ns);
+    } else {
+      attn_decode_combine<T, 64><<<rows, 256, 0, st>>>(partial, out, ns);
+    }
   } else {
     if (pos_dev) return hipErrorNotSupported;
     const int64_t waves = (int64_t)sh.bsz * sh.n_heads;

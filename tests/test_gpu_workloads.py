@@ -190,14 +190,15 @@ def test_determinism_batch_independence_causality():
     assert not torch.equal(o3[:, t], o1[:, t])
 
 
-@pytest.mark.parametrize("max_pos", [4000, 137])
+@pytest.mark.parametrize("max_pos", [4000, 1000, 137])
 @pytest.mark.parametrize("w", [SMALL, SMALL_ROWS], ids=lambda w: w.name)
 def test_decode_at_device_position_matches_oracle(w, max_pos):
     """llama_block_decode_at reads the position from device memory.  With a bound
-    above the actual position (max_start_pos 4000 or 137 while the steps run at
+    above the actual position (max_start_pos 4000, 1000 or 137 while the steps run at
     100..105) the attention splits are laid out for the bound's length, and the
-    later ones are empty; the outputs and the appended cache rows must still
-    follow the oracle's prefill + decode chain."""
+    later ones are empty (bound 1000: eight splits, merged by one wave per
+    row); the outputs and the appended cache rows must still follow the
+    oracle's prefill + decode chain."""
     from decoder_block_amd import _lib as L
     dev = need_gpu()
     a = w.prefill_len
