@@ -167,14 +167,23 @@ int block_forward_t(const Dims& g, const llama_model_args* a, const llama_block_
   else
     e = llama::attn_prefill<T>(q, ck, cv, o, sh, st);
   if (e != hipSuccess || mark(3) != hipSuccess) return LLAMA_ERR_HIP;
+  // 5..64 tokens in bf16 with wo split over K: the split reduction also applies
+  // the residual and computes ffn_norm's x * g and row factor (one pass over h)
+  const bool wo_norm = bf && !fused_norm && llama::gemm_residual_norm_fits(M, g.D, nq, nq);
   {
     llama::WeightRows<T> wr{(const T*)w->wo, nullptr, nullptr, g.D, g.D};
     llama::EpiResidual<T> epi{h, x, g.D};
-    e = llama::gemm_launch<T>(o, nq, wr, M, g.D, nq, epi, llama::gemm_pick_splits(M, g.D, nq, false, bf), part, st);
+    if constexpr (sizeof(T) == 2) {
+      if (wo_norm)
+        e = llama::gemm_residual_norm_launch(o, nq, (const T*)w->wo, M, g.D, nq, h, x, (const T*)w->ffn_norm, hn, r2,
+                                             a->norm_eps, part, st);
+    }
+    if (!wo_norm)
+      e = llama::gemm_launch<T>(o, nq, wr, M, g.D, nq, epi, llama::gemm_pick_splits(M, g.D, nq, false, bf), part, st);
     if (e != hipSuccess || mark(4) != hipSuccess) return LLAMA_ERR_HIP;
   }
   // out = h + w2(silu(w1 hn) * w3 hn), hn = RMSNorm(h)
-  if (!fused_norm) e = llama::rmsnorm<T>(h, g.D, (const T*)w->ffn_norm, hn, M, g.D, a->norm_eps, st, r2);
+  if (!fused_norm && !wo_norm) e = llama::rmsnorm<T>(h, g.D, (const T*)w->ffn_norm, hn, M, g.D, a->norm_eps, st, r2);
   if (e != hipSuccess || mark(5) != hipSuccess) return LLAMA_ERR_HIP;
   {
     if constexpr (sizeof(T) == 2) {

@@ -576,11 +576,58 @@ splitk_reduce(const float* __restrict__ partial, int splits, int M, int N, Epi e
   }
 }
 
+// Split-K reduction fused with the residual add and the next RMSNorm, one
+// 1024-thread workgroup per token row: y = r + sum_z partial[z] (rounded to the
+// output type), then yn = y * g and rscale[m] = rsqrt(mean(y^2) + eps) from the
+// rounded y, as the normalisation kernel would compute them from y in memory.
+// Every lane issues its splits' loads four at a time (clamped to the last
+// split, weighted 0 past the end).
+__global__ void __launch_bounds__(1024)
+reduce_residual_norm(const float* __restrict__ partial, int splits, int M, int N, const bf16* r, bf16* y,
+                     const bf16* __restrict__ g, bf16* __restrict__ yn, float* __restrict__ rscale, float eps) {
+  __shared__ float red[16];
+  const int m = blockIdx.x;
+  const int64_t row = (int64_t)m * N;
+  float ss = 0.f;
+  for (int n = threadIdx.x * 4; n < N; n += 1024 * 4) {
+    f32x4 s = load4(r + row + n);
+    for (int z0 = 0; z0 < splits; z0 += 4) {
+      f32x4 v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = *(const f32x4*)(partial + ((int64_t)min(z0 + i, splits - 1) * M + m) * N + n);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s += z0 + i < splits ? v[i] : f32x4{};
+    }
+    const bf16x4 yb = {(bf16)s[0], (bf16)s[1], (bf16)s[2], (bf16)s[3]};
+    *(bf16x4*)(y + row + n) = yb;
+    const f32x4 gv = load4(g + n);
+    f32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float f = (float)yb[i];
+      ss += f * f;
+      o[i] = f * gv[i];
+    }
+    store4(yn + row + n, o);
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tot += red[i];
+    rscale[m] = 1.0f / sqrtf(tot / (float)N + eps);
+  }
+}
+
 // ------------------------------------------------------------------ launch
 template <bool DUAL, class Epi>
 hipError_t launch_reduce(const float* partial, int splits, int M, int N, Epi epi, hipStream_t st) {
   const int64_t groups = (int64_t)M * (N / 4);
-  if (groups < 32768) {
+  // eight lanes per group when the groups are few or the splits many (more than
+  // one batch of loads per lane would serialise the walk)
+  if (groups < 32768 || splits > 4) {
     const int blocks = (int)((groups * 8 + kThreads - 1) / kThreads);
     splitk_reduce<DUAL, 8, Epi><<<blocks, kThreads, 0, st>>>(partial, splits, M, N, epi);
   } else {
@@ -677,6 +724,35 @@ hipError_t launch_f32(const float* A, int64_t lda, WeightRows<float> w, int M, i
 }
 
 }  // namespace
+
+bool gemm_residual_norm_fits(int M, int N, int K, int64_t lda) {
+  return M > kGemvMaxM && M <= 64 && N % 4 == 0 && lda % 8 == 0 && K % kSkinnyBK == 0 &&
+         gemm_pick_splits(M, N, K, false, true) > 1;
+}
+
+hipError_t gemm_residual_norm_launch(const bf16* A, int64_t lda, const bf16* w, int M, int N, int K, bf16* y,
+                                     const bf16* r, const bf16* g, bf16* yn, float* rscale, float eps,
+                                     float* partial, hipStream_t st) {
+  if (!gemm_residual_norm_fits(M, N, K, lda)) return hipErrorInvalidValue;
+  const int splits = gemm_pick_splits(M, N, K, false, true);
+  WeightRows<bf16> wr{w, nullptr, nullptr, N, N};
+  EpiResidual<bf16> epi{y, r, N};   // (type only: the splits write partials)
+  const int tiles = (N + 127) / 128;
+  int kps = (K + splits - 1) / splits;
+  kps = (kps + kSkinnyBK - 1) / kSkinnyBK * kSkinnyBK;
+  if ((int64_t)(splits - 1) * kps >= K) return hipErrorInvalidValue;
+  dim3 grid(tiles, 1, splits);
+  if (M <= 32)
+    gemm_bf16_dma<32, 128, kSkinnyBK, 1, 6, false, true, EpiResidual<bf16>, 4>
+        <<<grid, 256, 0, st>>>(A, lda, wr, M, N, K, kps, epi, partial);
+  else
+    gemm_bf16_dma<64, 128, kSkinnyBK, 2, 6, false, true, EpiResidual<bf16>, 4>
+        <<<grid, 256, 0, st>>>(A, lda, wr, M, N, K, kps, epi, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  reduce_residual_norm<<<M, 1024, 0, st>>>(partial, splits, M, N, r, y, g, yn, rscale, eps);
+  return hipGetLastError();
+}
 
 int gemm_pick_splits(int M, int N, int K, bool dual, bool is_bf16) {
   if (M > 64) {

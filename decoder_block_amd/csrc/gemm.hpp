@@ -177,6 +177,15 @@ hipError_t gemm_dual_launch(const T* A, int64_t lda, const T* w1, const T* w3, i
 // Split count the launch layer uses for an M x N x K problem (1 for large M).
 int gemm_pick_splits(int M, int N, int K, bool dual, bool bf16);
 
+// The residual projection of a decode-sized call (bf16, 5..64 token rows, split K)
+// with its reduction fused with the next RMSNorm: y = r + A W^T, then yn = y * g
+// and rscale[m] = rsqrt(mean(y^2) + eps) for the GEMM that consumes yn.  `partial`
+// is sized as for gemm_launch.  Only valid where gemm_residual_norm_fits.
+bool gemm_residual_norm_fits(int M, int N, int K, int64_t lda);
+hipError_t gemm_residual_norm_launch(const bf16* A, int64_t lda, const bf16* w, int M, int N, int K, bf16* y,
+                                     const bf16* r, const bf16* g, bf16* yn, float* rscale, float eps,
+                                     float* partial, hipStream_t st);
+
 // Weight-streaming kernels for M <= kGemvMaxM token rows in bf16 (gemv.hip);
 // gemm_launch routes such problems there by itself.  They need N % 4 == 0,
 // K % 8 == 0 and lda % 8 == 0 (gemv_fits); for the QKV map, n1 and n2 must be

@@ -138,6 +138,10 @@ SMALL_ROWS = wl.Workload(31, "small-gqa-8kv", "bf16", 2048, 16, 8, 1536, 256, 0.
 # ragged chunks, and a single kv head serves all five query heads
 RAGGED4 = wl.Workload(32, "ragged-640-b4", "bf16", 640, 5, 1, 1712, 8, None, 1e-5, 1e4, batch=4, prefill_len=45,
                       decode_steps=4)
+# six tokens per decode step: the split-K projections of the tiled kernels, with
+# wo's split reduction fused with the residual add and ffn_norm
+SMALL_ROWS6 = wl.Workload(34, "small-gqa-8kv-b6", "bf16", 2048, 16, 8, 1536, 256, 0.25, 1e-5, 5e5, batch=6,
+                          prefill_len=100, decode_steps=4)
 RAGGED1 = wl.Workload(33, "ragged-640-b1", "bf16", 640, 5, 1, 1712, 8, None, 1e-5, 1e4, batch=1, prefill_len=45,
                       decode_steps=4)
 
@@ -146,7 +150,7 @@ def _small_runner(dev, batch=None, w=SMALL):
     return BlockRunner(model_args_for(w, max_batch=batch or w.batch), wl.block_weights(w), torch.bfloat16, dev)
 
 
-@pytest.mark.parametrize("w", [SMALL, SMALL_ROWS, RAGGED4, RAGGED1], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [SMALL, SMALL_ROWS, SMALL_ROWS6, RAGGED4, RAGGED1], ids=lambda w: w.name)
 def test_decode_chain_matches_prefill_and_oracle(w):
     dev = need_gpu()
     print(f"case {w.name}: prefill + decode chain + chunked prefill", flush=True)
