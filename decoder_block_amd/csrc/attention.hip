@@ -316,8 +316,8 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
 }
 
 // ------------------------------------------------------------------ decode (bf16 MFMA, split-K)
-template <int HD>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int HD, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const bf16* __restrict__ cv,
                  bf16* __restrict__ out, float* __restrict__ partial, AttnShape sh, int nsplit, int L,
                  float scale_log2, const int32_t* __restrict__ pos_dev) {
@@ -325,9 +325,10 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
   static_assert(HD == 64 || HD == 128, "head_dim");
   constexpr int RPI = 64 / CH;                // K rows per load instruction (whole rows)
   constexpr int KL = 32 / RPI;                // K loads per lane per 32-key chunk
-  __shared__ bf16x8 Vt[4][HD * 4];          // per wave: [d][4 chunks of 8 permuted keys]
-  __shared__ bf16x8 Kt[4][32 * CH];         // per wave: [key][chunk ^ ksw(key)]
-  __shared__ float mrg_m[4][16], mrg_l[4][16];
+  constexpr int CSTR = NW * 32;              // key stride between a wave's chunks
+  __shared__ bf16x8 Vt[NW][HD * 4];         // per wave: [d][4 chunks of 8 permuted keys]
+  __shared__ bf16x8 Kt[NW][32 * CH];        // per wave: [key][chunk ^ ksw(key)]
+  __shared__ float mrg_m[NW][16], mrg_l[NW][16];
 
   const int H = sh.n_heads, Hkv = sh.n_kv_heads;
   const int n_rep = H / Hkv;
@@ -473,27 +474,27 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
   };
 
   const int c_first = t_begin + wave * 32;
-  const int nit = c_first < t_end ? (t_end - c_first + 127) / 128 : 0;
+  const int nit = c_first < t_end ? (t_end - c_first + CSTR - 1) / CSTR : 0;
   bf16x8 kA[KL], vA[8], kB[KL], vB[8];
   if (nit > 0) load(c_first, kA, vA);
   int it = 0;
   // (the scheduling barriers keep each prefetch ahead of the compute that
   // would otherwise be hoisted above it and wait for every load in flight)
   for (; it + 1 < nit; it += 2) {
-    load(c_first + (it + 1) * 128, kB, vB);
+    load(c_first + (it + 1) * CSTR, kB, vB);
     __builtin_amdgcn_sched_barrier(0);
-    compute(c_first + it * 128, kA, vA);
+    compute(c_first + it * CSTR, kA, vA);
     __builtin_amdgcn_sched_barrier(0);
-    load(c_first + (it + 2) * 128, kA, vA);   // past the end: clamped rows, never used
+    load(c_first + (it + 2) * CSTR, kA, vA);   // past the end: clamped rows, never used
     __builtin_amdgcn_sched_barrier(0);
-    compute(c_first + (it + 1) * 128, kB, vB);
+    compute(c_first + (it + 1) * CSTR, kB, vB);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (it < nit) compute(c_first + it * 128, kA, vA);
+  if (it < nit) compute(c_first + it * CSTR, kA, vA);
 
-  // merge the four waves' (max, sum, o) in LDS
+  // merge the NW waves' (max, sum, o) in LDS
   __syncthreads();
-  float* obuf = (float*)&Vt[0][0];            // [4 waves][16 heads][HD] floats
+  float* obuf = (float*)&Vt[0][0];            // [NW waves][16 heads][HD] floats
   if (g == 0) {
     mrg_m[wave][l16] = m_run;
     mrg_l[wave][l16] = l_run;
@@ -504,16 +505,16 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
     for (int v = 0; v < 4; ++v) obuf[(wave * 16 + l16) * HD + dt * 16 + g * 4 + v] = oacc[dt][v];
   __syncthreads();
 
-  const int hh = tid >> 4;                    // head slot 0..15
+  const int hh = tid >> 4;                    // head slot 0..15 (the first 256 threads)
   const int d0 = (tid & 15) * (HD / 16);
   const int hl2 = hg * 16 + hh;
-  if (hl2 >= n_rep) return;
+  if (tid >= 256 || hl2 >= n_rep) return;
   float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) M = fmaxf(M, mrg_m[w][hh]);
-  float wt[4], Ls = 0.f;
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, mrg_m[w][hh]);
+  float wt[NW], Ls = 0.f;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     wt[w] = mrg_m[w][hh] == -INFINITY ? 0.f : exp2f(mrg_m[w][hh] - M);
     Ls += wt[w] * mrg_l[w][hh];
   }
@@ -522,7 +523,7 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
   for (int k = 0; k < HD / 16; ++k) {
     float acc = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) acc += wt[w] * obuf[(w * 16 + hh) * HD + d0 + k];
+    for (int w = 0; w < NW; ++w) acc += wt[w] * obuf[(w * 16 + hh) * HD + d0 + k];
     o[k] = acc;
   }
   const int hq = j * n_rep + hl2;
@@ -689,7 +690,16 @@ hipError_t attn_prefill(const T* q, const T* cache_k, const T* cache_v, T* out, 
   return hipGetLastError();
 }
 
+static int attn_decode_waves(int bsz, int n_heads, int n_kv_heads) {
+  // one 8-wave workgroup per (sequence, kv group) when those units alone fill
+  // between half and all of the CUs (one resident round at one workgroup per CU):
+  // no split, no merge kernel
+  const int units = bsz * n_kv_heads * ((n_heads / n_kv_heads + 15) / 16);
+  return units >= kResidentDecodeWgs / 4 && units <= kResidentDecodeWgs / 2 ? 8 : 4;
+}
+
 int attn_decode_splits(int bsz, int n_heads, int n_kv_heads, int T) {
+  if (attn_decode_waves(bsz, n_heads, n_kv_heads) == 8) return 1;
   const int n_rep = n_heads / n_kv_heads;
   const int units = bsz * n_kv_heads * ((n_rep + 15) / 16);
   // two rounds of the 512 workgroups that are resident at once (two per CU);
@@ -716,12 +726,19 @@ hipError_t attn_decode(const T* q, const T* cache_k, const T* cache_v, T* out, c
     L = (L + 31) / 32 * 32;
     const int n_rep = sh.n_heads / sh.n_kv_heads;
     dim3 grid(sh.n_kv_heads * ((n_rep + 15) / 16), ns, sh.bsz);
-    if (sh.head_dim == 128)
-      attn_decode_mfma<128><<<grid, 256, 0, st>>>(q, cache_k, cache_v, out, partial, sh, ns, L, scale * kLog2e,
-                                                  pos_dev);
+    const bool w8 = attn_decode_waves(sh.bsz, sh.n_heads, sh.n_kv_heads) == 8;
+    if (sh.head_dim == 128 && w8)
+      attn_decode_mfma<128, 8><<<grid, 512, 0, st>>>(q, cache_k, cache_v, out, partial, sh, ns, L, scale * kLog2e,
+                                                     pos_dev);
+    else if (sh.head_dim == 128)
+      attn_decode_mfma<128, 4><<<grid, 256, 0, st>>>(q, cache_k, cache_v, out, partial, sh, ns, L, scale * kLog2e,
+                                                     pos_dev);
+    else if (w8)
+      attn_decode_mfma<64, 8><<<grid, 512, 0, st>>>(q, cache_k, cache_v, out, partial, sh, ns, L, scale * kLog2e,
+                                                    pos_dev);
     else
-      attn_decode_mfma<64><<<grid, 256, 0, st>>>(q, cache_k, cache_v, out, partial, sh, ns, L, scale * kLog2e,
-                                                 pos_dev);
+      attn_decode_mfma<64, 4><<<grid, 256, 0, st>>>(q, cache_k, cache_v, out, partial, sh, ns, L, scale * kLog2e,
+                                                    pos_dev);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1) return e;
     const int rows = sh.bsz * sh.n_heads;

@@ -185,6 +185,8 @@ def test_attn_prefill(dtype, B, S, p0, H, Hkv, d):
     ("bf16", 2, 999, 4, 1, 64),      # MQA head_dim 64
     ("bf16", 1, 500, 32, 1, 128),    # n_rep 32 (two head groups)
     ("bf16", 2, 300, 8, 2, 64),      # three splits, head_dim 64 (one-wave merge)
+    ("bf16", 16, 1500, 16, 8, 128),  # 128 (sequence, kv head) units: one 8-wave workgroup each, no split
+    ("bf16", 64, 700, 8, 4, 64),     # 256 units, head_dim 64, 8 waves
     ("f32", 2, 79, 8, 2, 32),
 ])
 def test_attn_decode(dtype, B, p0, H, Hkv, d):
