@@ -277,6 +277,11 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
   const int m0 = tm * BM, n0 = tn * BN_OUT;
   const int kb = blockIdx.z * k_per_split;
   const int nk = (min(K, kb + k_per_split) - kb) / BK;
+  // Small-M tiles walk their k-tiles in a rotated order, starting at k-tile
+  // tn % nk: weight rows a power of two apart (K = 4096, 8192) read at the same
+  // k offset by every concurrent workgroup fall on few HBM channels (a probe of
+  // this read pattern over 16 KiB rows: 4.3 TB/s in step, 5.4 TB/s rotated).
+  const int krot = (BM <= 64 && nk > 0) ? tn % nk : 0;
 
   // bank-group swizzle of the 16-byte chunks: a ds_read_b128 phase reads one
   // chunk of 16 consecutive rows, which must hit 16 distinct bank groups
@@ -314,7 +319,8 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
   // refill at the end of the loop stays branch-free; those copies are never read)
   auto issue = [&](int kt) {
     const int st = kt % NS;
-    const int kc = min(kt, nk - 1);
+    int kc = min(kt, nk - 1) + krot;
+    kc = kc >= nk ? kc - nk : kc;
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
       LLAMA_LDS void* dst = (LLAMA_LDS void*)&smem[st][blk_of(i) * 64];
