@@ -177,6 +177,29 @@ def test_attn_prefill(dtype, B, S, p0, H, Hkv, d):
     check(out, ref, dtype, "attn prefill")
 
 
+def test_attn_prefill_sequences_in_cache_sized_groups():
+    """Three 8200-token sequences of GQA 32/16 attend 67 MB of K/V each: more
+    than the prefill kernel takes in one dispatch group (192 MiB), so it runs
+    the sequences as a group of two, then a group of one.  Sampled query rows
+    (first and last of several 64-position query blocks) against the oracle."""
+    need_gpu()
+    B, S, H, Hkv, d = 3, 8200, 32, 16, 128
+    print(f"case attn_prefill grouped B={B} S={S} H={H} Hkv={Hkv} d={d}", flush=True)
+    args = _args(H, Hkv, d, B + 1, S + 3)
+    q = rnd((B, S, H, d), 1.0)
+    k = rnd((B, S, Hkv, d), 1.0)
+    v = rnd((B, S, Hkv, d), 1.0)
+    gck = torch.zeros(B + 1, S + 3, Hkv, d, dtype=torch.bfloat16, device="cuda:0")
+    gcv = torch.zeros_like(gck)
+    out = torch.empty(B, S, H * d, dtype=torch.bfloat16, device="cuda:0")
+    dba.llama_gqa_attn_prefill(dev(q), dev(k), dev(v), gck, gcv, out, args, B, S, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(gck[:B, :S].cpu(), k) and torch.equal(gcv[:B, :S].cpu(), v)   # the append: a copy
+    rows = [0, 1, 63, 64, 2047, 4100, 8135, 8199]
+    ref = ob.gqa_attention(f64(q), f64(k), f64(v), 0, rows)
+    check(out[:, rows], ref, "bf16", "attn prefill, sequences in groups")
+
+
 @pytest.mark.parametrize("dtype,B,p0,H,Hkv,d", [
     ("bf16", 3, 0, 8, 2, 128),       # single key
     ("bf16", 2, 40, 8, 8, 128),      # MHA, short
