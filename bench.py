@@ -182,9 +182,13 @@ def cpu_baseline(w, wts, x):
     import numpy as np
     import torch
     from oracle import block as ob
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max((i.get("num_threads", 1) for i in libs), default=1)
+        if libs:
+            blas = f"{libs[0].get('internal_api', '?')} {libs[0].get('version', '')}".strip()
     except Exception:
         cores = os.cpu_count() or 1
     S, B = w.prefill_len, w.batch
@@ -196,7 +200,20 @@ def cpu_baseline(w, wts, x):
     ob.block_forward(xs, W, ck, cv, 0, w.n_heads, w.n_kv_heads, w.norm_eps, w.rope_theta)
     dt = time.perf_counter() - t0
     return {"value": B * S / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"the whole {w.name} workload ({B} x {S}-token prefill), numpy float64, {dt:.1f} s"}
+            "sample": f"the whole {w.name} workload ({B} x {S}-token prefill), numpy float64, {dt:.1f} s",
+            "blas": blas, "cpu": cpu_model()}
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_decode_step_us(w, wts, x, cache_k, cache_v, p0):
