@@ -101,6 +101,23 @@ def test_rope_apply(dtype):
 ])
 def test_linear(dtype, M, K, N):
     need_gpu()
+    _linear_case(dtype, M, K, N)
+
+
+def test_linear_seeded_shapes():
+    """Twenty-four projection shapes from a seeded generator: 1-4 rows (weight
+    streams), 5-64 (small-M tiles, split over K when the grid is short) and
+    65-400 rows (large tiles), K a multiple of 8 up to 3072, N of 4 up to 1200."""
+    need_gpu()
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(4243)))
+    for i in range(24):
+        M = int(g.integers(1, 5) if i % 3 == 0 else (g.integers(5, 65) if i % 3 == 1 else g.integers(65, 401)))
+        K = 8 * int(g.integers(1, 385))
+        N = 4 * int(g.integers(1, 301))
+        _linear_case("bf16", M, K, N)
+
+
+def _linear_case(dtype, M, K, N):
     print(f"case linear {dtype} M={M} K={K} N={N}", flush=True)
     x = rnd((M, K), 1.0, dtype)
     w = rnd((N, K), 0.05, dtype)
@@ -121,6 +138,22 @@ def test_linear(dtype, M, K, N):
     ("bf16", 1, 512, 1536), ("bf16", 4, 640, 1712), ("bf16", 2, 4096, 14336)])
 def test_swiglu_ffn(dtype, rows, dim, hidden):
     need_gpu()
+    _swiglu_case(dtype, rows, dim, hidden)
+
+
+def test_swiglu_ffn_seeded_shapes():
+    """Twelve FFN shapes from a seeded generator: 1-4, 5-64 and 65-200 rows, dim
+    and hidden multiples of 8 (64-1600 and 128-3200)."""
+    need_gpu()
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(4244)))
+    for i in range(12):
+        rows = int(g.integers(1, 5) if i % 3 == 0 else (g.integers(5, 65) if i % 3 == 1 else g.integers(65, 201)))
+        dim = 8 * int(g.integers(8, 201))
+        hidden = 8 * int(g.integers(16, 401))
+        _swiglu_case("bf16", rows, dim, hidden)
+
+
+def _swiglu_case(dtype, rows, dim, hidden):
     print(f"case swiglu {dtype} rows={rows} dim={dim} hidden={hidden}", flush=True)
     x = rnd((rows, dim), 1.0, dtype)
     w1, w3 = rnd((hidden, dim), 0.05, dtype), rnd((hidden, dim), 0.05, dtype)
@@ -214,6 +247,30 @@ def test_attn_prefill_sequences_in_cache_sized_groups():
 ])
 def test_attn_decode(dtype, B, p0, H, Hkv, d):
     need_gpu()
+    _attn_decode_case(dtype, B, p0, H, Hkv, d)
+
+
+def test_attn_decode_seeded_shapes():
+    """Twenty decode shapes drawn from a seeded generator (batch 1-64, 0-3000
+    cached keys, 1-8 kv heads, n_rep 1-32, head_dim 64/128): they land on every
+    grid rule of the decode kernel (one split, merged by one wave per row or by
+    four, one 8-wave workgroup per unit)."""
+    need_gpu()
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(4242)))
+    for _ in range(20):
+        Hkv = int(g.choice([1, 2, 4, 8]))
+        n_rep = int(g.choice([1, 2, 4, 8, 16, 32]))
+        while Hkv * n_rep > 64:
+            n_rep //= 2
+        d = int(g.choice([64, 128]))
+        B = int(g.integers(1, 65))
+        # keep the oracle's expanded float64 cache under ~400 MB
+        p0_max = max(1, min(3000, int(5e7 // (B * Hkv * n_rep * d))))
+        p0 = int(g.integers(0, p0_max + 1))
+        _attn_decode_case("bf16", B, p0, Hkv * n_rep, Hkv, d)
+
+
+def _attn_decode_case(dtype, B, p0, H, Hkv, d):
     print(f"case attn_decode {dtype} B={B} p0={p0} H={H} Hkv={Hkv} d={d}", flush=True)
     maxS = p0 + 2
     args = _args(H, Hkv, d, B, maxS)
