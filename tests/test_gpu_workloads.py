@@ -125,6 +125,44 @@ def test_llama2_70b_block_decode_batch32():
     np.testing.assert_array_equal(f64(run.cache_k[:, :p]), f64(ck0[:, :p]))
 
 
+def test_block_decode_seeded_shapes():
+    """Ten one-token block calls with shapes from a seeded generator (head_dim
+    64/128, 1-8 kv heads, n_rep 1-8, batch 1-80 over 1-1500 cached N(0,1) rows):
+    weight streams with the norms fused (1-4 tokens), small-M tiles with wo's
+    split reduction fused with ffn_norm (5-64), large tiles beyond; outputs and
+    the appended cache rows against the oracle."""
+    dev = need_gpu()
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(4245)))
+    for i in range(10):
+        d = int(g.choice([64, 128]))
+        Hkv = int(g.choice([1, 2, 4, 8]))
+        n_rep = int(g.choice([1, 2, 4, 8]))
+        while Hkv * n_rep * d > 4096:
+            n_rep //= 2
+        H = Hkv * n_rep
+        D = H * d
+        mo = int(g.choice([8, 64, 256]))
+        F = mo * -(-int(8 * D / 3) // mo)
+        B = int(g.integers(1, 5) if i % 3 == 0 else (g.integers(5, 65) if i % 3 == 1 else g.integers(65, 81)))
+        p0 = int(g.integers(1, 1501))
+        w = wl.Workload(200 + i, f"seeded-{i}", "bf16", D, H, Hkv, F, mo, None, 1e-5, 1e4, batch=B, prefill_len=0,
+                        decode_steps=1, cache_prefill=p0)
+        print(f"case {w.name}: D={D} H={H} Hkv={Hkv} d={d} F={F} B={B} decode at {p0}", flush=True)
+        wts = wl.block_weights(w)
+        x = wl.activations(w)
+        ck0, cv0 = wl.prefilled_cache(w)
+        run = BlockRunner(model_args_for(w), wts, torch.bfloat16, dev, cache=(ck0, cv0))
+        out = run.forward(x.to(dev), p0)
+        torch.cuda.synchronize()
+        ck, cv = f64(ck0), f64(cv0)
+        ref = ob.block_forward(f64(x), _w64(wts), ck, cv, p0, H, Hkv, w.norm_eps, w.rope_theta)
+        check(out, ref, "bf16", f"{w.name} decode outputs")
+        check(run.cache_k[:, p0], ck[:, p0], "bf16", f"{w.name} appended k")
+        check(run.cache_v[:, p0], cv[:, p0], "bf16", f"{w.name} appended v")
+        del run
+        torch.cuda.empty_cache()
+
+
 # ----------------------------------------------------------------------------- invariants
 SMALL = wl.Workload(30, "small-gqa", "bf16", 512, 8, 2, 1536, 256, None, 1e-5, 1e4, batch=3, prefill_len=100,
                     decode_steps=6)
