@@ -163,6 +163,45 @@ def test_block_decode_seeded_shapes():
         torch.cuda.empty_cache()
 
 
+def test_block_prefill_seeded_shapes():
+    """Eight block prefill calls with shapes from a seeded generator (head_dim
+    64/128, 1-8 kv heads, n_rep 1-8, batch 1-4, 5-700 new tokens after 0-500
+    cached N(0,1) rows): ragged token counts on every GEMM tile family, the
+    attention's head grouping and causal offsets; outputs and the appended cache
+    rows against the oracle."""
+    dev = need_gpu()
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(4246)))
+    for i in range(8):
+        d = int(g.choice([64, 128]))
+        Hkv = int(g.choice([1, 2, 4, 8]))
+        n_rep = int(g.choice([1, 2, 4, 8]))
+        while Hkv * n_rep * d > 2048:
+            n_rep //= 2
+        H = Hkv * n_rep
+        D = H * d
+        mo = int(g.choice([8, 64, 256]))
+        F = mo * -(-int(8 * D / 3) // mo)
+        B = int(g.integers(1, 5))
+        S = int(g.integers(5, 701))
+        p0 = int(g.choice([0, int(g.integers(1, 501))]))
+        w = wl.Workload(300 + i, f"seeded-prefill-{i}", "bf16", D, H, Hkv, F, mo, None, 1e-5, 1e4, batch=B,
+                        prefill_len=S, decode_steps=0, cache_prefill=p0)
+        print(f"case {w.name}: D={D} H={H} Hkv={Hkv} d={d} F={F} B={B} S={S} at {p0}", flush=True)
+        wts = wl.block_weights(w)
+        x = wl.activations(w)[:, :S].contiguous()
+        ck0, cv0 = wl.prefilled_cache(w)
+        run = BlockRunner(model_args_for(w), wts, torch.bfloat16, dev, cache=(ck0, cv0))
+        out = run.forward(x.to(dev), p0)
+        torch.cuda.synchronize()
+        ck, cv = f64(ck0), f64(cv0)
+        ref = ob.block_forward(f64(x), _w64(wts), ck, cv, p0, H, Hkv, w.norm_eps, w.rope_theta)
+        check(out, ref, "bf16", f"{w.name} outputs")
+        check(run.cache_k[:, p0:p0 + S], ck[:, p0:p0 + S], "bf16", f"{w.name} appended k")
+        check(run.cache_v[:, p0:p0 + S], cv[:, p0:p0 + S], "bf16", f"{w.name} appended v")
+        del run
+        torch.cuda.empty_cache()
+
+
 # ----------------------------------------------------------------------------- invariants
 SMALL = wl.Workload(30, "small-gqa", "bf16", 512, 8, 2, 1536, 256, None, 1e-5, 1e4, batch=3, prefill_len=100,
                     decode_steps=6)
