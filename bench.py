@@ -230,6 +230,89 @@ def cpu_decode_step_us(w, wts, x, cache_k, cache_v, p0):
     return (time.perf_counter() - t0) * 1e6
 
 
+def bench_tiny(dev, cpu):
+    """The tiny fp32 workload (dim 256, GQA 8/2, one 64-token prompt, then 16 one-token
+    calls): launch-latency bound, so absolute microseconds per call."""
+    import numpy as np
+    import torch
+    import workloads as wl
+    from decoder_block_amd.runner import BlockRunner, model_args_for
+    w = wl.WORKLOADS[1]
+    wts = wl.block_weights(w)
+    r = BlockRunner(model_args_for(w), wts, torch.float32, dev)
+    x = wl.activations(w).to(dev)
+    S = w.prefill_len
+    xp = x[:, :S].contiguous()
+    xs = [x[:, S + t:S + t + 1].contiguous() for t in range(w.decode_steps)]
+    for _ in range(10):                        # untimed: code loading, clocks
+        r.forward(xp, 0)
+    torch.cuda.synchronize()
+    pre = []
+    for _ in range(20):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        r.forward(xp, 0)
+        e1.record()
+        torch.cuda.synchronize()
+        pre.append(e0.elapsed_time(e1) * 1e3)
+    dec = []
+    for t, xt in enumerate(xs):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        r.forward(xt, S + t)
+        e1.record()
+        torch.cuda.synchronize()
+        dec.append(e0.elapsed_time(e1) * 1e3)
+    res = {"prefill_us_median": round(pct(pre, 0.5), 1), "decode_step_us_median": round(pct(dec, 0.5), 1),
+           "decode_steps": len(dec), "dtype": "f32"}
+    if cpu:
+        from oracle import block as ob
+        W = {k: v.to(torch.float64).numpy() for k, v in wts.items()}
+        xc = x.cpu().to(torch.float64).numpy()
+        shape = (1, w.max_seq_len, w.n_kv_heads, w.head_dim)
+        ck, cv = np.zeros(shape), np.zeros(shape)
+        t0 = time.perf_counter()
+        ob.block_forward(xc[:, :S], W, ck, cv, 0, w.n_heads, w.n_kv_heads, w.norm_eps, w.rope_theta)
+        t1 = time.perf_counter()
+        ob.block_forward(xc[:, S:S + 1], W, ck, cv, S, w.n_heads, w.n_kv_heads, w.norm_eps, w.rope_theta)
+        t2 = time.perf_counter()
+        res["cpu_oracle_prefill_us"] = round((t1 - t0) * 1e6, 1)
+        res["cpu_oracle_decode_step_us"] = round((t2 - t1) * 1e6, 1)
+    return res
+
+
+def stack_oracle_sample(w):
+    """The oracle on a bounded sample of the 32-layer workload: sequence 0 of 64,
+    layers 0 and 1 (weights generated and upcast layer by layer), its 2048-token
+    prompt and then one one-token call; rates scaled to 32 layers."""
+    import numpy as np
+    import torch
+    import workloads as wl
+    from oracle import block as ob
+    emb, _, _ = wl.stack_tensors(w)
+    tok = wl.prompt_tokens(w)[0:1]
+    h = emb[tok].to(torch.float64).numpy()                 # [1, S, D]
+    hd = emb[tok[:, -1:]].to(torch.float64).numpy()        # stand-in for the next token's row
+    S = w.prefill_len
+    shape = (1, S + 1, w.n_kv_heads, w.head_dim)
+    t_pre = t_dec = 0.0
+    layers = 2
+    for l in range(layers):
+        W = {k: v.to(torch.float64).numpy() for k, v in wl.block_weights(w, l).items()}
+        ck, cv = np.zeros(shape), np.zeros(shape)
+        t0 = time.perf_counter()
+        h = ob.block_forward(h, W, ck, cv, 0, w.n_heads, w.n_kv_heads, w.norm_eps, w.rope_theta)
+        t1 = time.perf_counter()
+        hd = ob.block_forward(hd, W, ck, cv, S, w.n_heads, w.n_kv_heads, w.norm_eps, w.rope_theta)
+        t2 = time.perf_counter()
+        t_pre += t1 - t0
+        t_dec += t2 - t1
+    scale = w.n_layers / layers
+    return {"prefill_tokens_per_s": round(S / (t_pre * scale), 2), "decode_ms_per_step": round(t_dec * scale * 1e3, 1),
+            "kind": "oracle", "sample": f"sequence 0 of {w.batch}, layers 0-1 of {w.n_layers} (times scaled to "
+            f"{w.n_layers} layers; embedding and output projection not included), numpy float64"}
+
+
 def bench_stack(dev, steps):
     """32 layers + embedding + LM head: prefill of 64 x 2048 prompts, then greedy one-token steps."""
     import torch
@@ -439,8 +522,15 @@ def main():
                                        "same shape (its cost depends on the shape only)")
         extra.update({"llama3_8b_prefill_8192": pre3, "llama3_8b_decode": dec3, "llama2_70b_decode_b32": dec4})
 
+    if not a.prefill_only:
+        log("workload tiny-f32: 64-token prefill, then one-token calls")
+        extra["tiny_f32"] = bench_tiny(dev, not a.no_cpu_baseline)
+
     if a.stack:
         extra["llama3_8b_stack"] = bench_stack(dev, a.decode_steps)
+        if not a.no_cpu_baseline:
+            log("cpu oracle: bounded sample of the 32-layer stack")
+            extra["llama3_8b_stack"]["cpu_oracle"] = stack_oracle_sample(wl.WORKLOADS[5])
 
     cpu = None
     if not a.no_cpu_baseline:
