@@ -141,19 +141,17 @@ int block_forward_t(const Dims& g, const llama_model_args* a, const llama_block_
   // h = x + wo(attention(RMSNorm(x))).  RMSNorm(x) W^T is computed as
   // rsqrt(mean(x^2) + eps) * ((x * g) W^T): the row factor is applied to the fp32
   // accumulators, so the normalised activation is never rounded to bf16.
-  // Up to four tokens in bf16: the weight-streaming kernels take the un-normalised
+  // Up to four tokens: the weight-streaming kernels take the un-normalised
   // rows and apply the same factor themselves, so no normalisation pass runs.
-  const bool fused_norm = bf && llama::gemv_fits(M, nq + 2 * nkv, g.D, g.D) && llama::gemv_fits(M, g.F, g.D, g.D);
+  const bool fused_norm = llama::gemv_fits<T>(M, nq + 2 * nkv, g.D, g.D) && llama::gemv_fits<T>(M, g.F, g.D, g.D);
   if (!fused_norm) e = llama::rmsnorm<T>(x, g.D, (const T*)w->attention_norm, xn, M, g.D, a->norm_eps, st, r1);
   if (e != hipSuccess || mark(1) != hipSuccess) return LLAMA_ERR_HIP;
   {
     llama::WeightRows<T> wr{(const T*)w->wq, (const T*)w->wk, (const T*)w->wv, nq, nq + nkv};
     const int N = nq + 2 * nkv;
-    if constexpr (sizeof(T) == 2) {
-      if (fused_norm) {
-        llama::EpiQKV<T> epi{q, ck, cv, freqs, seqlen, start_pos, a->max_seq_len, nq, nkv, g.d, nullptr, pos_dev};
-        e = llama::gemv_launch(x, g.D, wr, M, N, g.D, (const T*)w->attention_norm, a->norm_eps, epi, st);
-      }
+    if (fused_norm) {
+      llama::EpiQKV<T> epi{q, ck, cv, freqs, seqlen, start_pos, a->max_seq_len, nq, nkv, g.d, nullptr, pos_dev};
+      e = llama::gemv_launch<T>(x, g.D, wr, M, N, g.D, (const T*)w->attention_norm, a->norm_eps, epi, st);
     }
     if (!fused_norm) {
       llama::EpiQKV<T> epi{q, ck, cv, freqs, seqlen, start_pos, a->max_seq_len, nq, nkv, g.d, r1, pos_dev};
@@ -186,12 +184,10 @@ int block_forward_t(const Dims& g, const llama_model_args* a, const llama_block_
   if (!fused_norm && !wo_norm) e = llama::rmsnorm<T>(h, g.D, (const T*)w->ffn_norm, hn, M, g.D, a->norm_eps, st, r2);
   if (e != hipSuccess || mark(5) != hipSuccess) return LLAMA_ERR_HIP;
   {
-    if constexpr (sizeof(T) == 2) {
-      if (fused_norm) {
-        llama::EpiSwiGLU<T> epi{gt, g.F, nullptr};
-        e = llama::gemv_dual_launch(h, g.D, (const T*)w->w1, (const T*)w->w3, M, g.F, g.D, (const T*)w->ffn_norm,
-                                    a->norm_eps, epi, st);
-      }
+    if (fused_norm) {
+      llama::EpiSwiGLU<T> epi{gt, g.F, nullptr};
+      e = llama::gemv_dual_launch<T>(h, g.D, (const T*)w->w1, (const T*)w->w3, M, g.F, g.D, (const T*)w->ffn_norm,
+                                     a->norm_eps, epi, st);
     }
     if (!fused_norm) {
       llama::EpiSwiGLU<T> epi{gt, g.F, r2};

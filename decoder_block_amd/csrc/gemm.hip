@@ -776,7 +776,7 @@ int gemm_pick_splits(int M, int N, int K, bool dual, bool is_bf16) {
   }
   // up to four tokens: the weight-streaming kernel, one pass over K
   // (gemm_launch sends the problem there when its shapes allow)
-  if (is_bf16 && gemv_fits(M, N, K, K)) return 1;
+  if (is_bf16 ? gemv_fits<bf16>(M, N, K, K) : gemv_fits<float>(M, N, K, K)) return 1;
   // small token count: the weights stream from HBM once; split K so that the
   // grid covers the CUs
   if (is_bf16 && K % kSkinnyBK == 0) {
@@ -813,11 +813,11 @@ template <typename T, class Epi>
 hipError_t gemm_launch(const T* A, int64_t lda, WeightRows<T> w, int M, int N, int K, Epi epi,
                        int splits, float* partial, hipStream_t st) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  if constexpr (sizeof(T) == 2) {
-    if (gemv_fits(M, N, K, lda) && w.n1 % 4 == 0 && w.n2 % 4 == 0)
-      return gemv_launch<Epi>(A, lda, w, M, N, K, nullptr, 0.0f, epi, st);
+  if (gemv_fits<T>(M, N, K, lda) && w.n1 % 4 == 0 && w.n2 % 4 == 0)
+    return gemv_launch<T, Epi>(A, lda, w, M, N, K, nullptr, 0.0f, epi, st);
+  if constexpr (sizeof(T) == 2)
     return launch_bf16<false>(A, lda, w, M, N, K, epi, splits, partial, st);
-  } else
+  else
     return launch_f32<false>(A, lda, w, M, N, K, epi, splits, partial, st);
 }
 
@@ -826,10 +826,10 @@ hipError_t gemm_dual_launch(const T* A, int64_t lda, const T* w1, const T* w3, i
                             Epi epi, int splits, float* partial, hipStream_t st) {
   if (M <= 0 || N <= 0) return hipSuccess;
   WeightRows<T> w{w1, w3, nullptr, N, N};
-  if constexpr (sizeof(T) == 2) {
-    if (gemv_fits(M, N, K, lda)) return gemv_dual_launch<Epi>(A, lda, w1, w3, M, N, K, nullptr, 0.0f, epi, st);
+  if (gemv_fits<T>(M, N, K, lda)) return gemv_dual_launch<T, Epi>(A, lda, w1, w3, M, N, K, nullptr, 0.0f, epi, st);
+  if constexpr (sizeof(T) == 2)
     return launch_bf16<true>(A, lda, w, M, N, K, epi, splits, partial, st);
-  } else
+  else
     return launch_f32<true>(A, lda, w, M, N, K, epi, splits, partial, st);
 }
 

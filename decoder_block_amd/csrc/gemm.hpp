@@ -186,19 +186,21 @@ hipError_t gemm_residual_norm_launch(const bf16* A, int64_t lda, const bf16* w, 
                                      const bf16* r, const bf16* g, bf16* yn, float* rscale, float eps,
                                      float* partial, hipStream_t st);
 
-// Weight-streaming kernels for M <= kGemvMaxM token rows in bf16 (gemv.hip);
-// gemm_launch routes such problems there by itself.  They need N % 4 == 0,
-// K % 8 == 0 and lda % 8 == 0 (gemv_fits); for the QKV map, n1 and n2 must be
-// multiples of 4 as well.  With norm_w set, A's rows are RMS-normalised on the
-// fly (A * norm_w in the products, rsqrt(mean(A^2) + eps) on the accumulators);
-// the epilogue's own rscale must then be null.
+// Weight-streaming kernels for M <= kGemvMaxM token rows in bf16 or fp32
+// (gemv.hip); gemm_launch routes such problems there by itself.  They need
+// N % 4 == 0 and K, lda multiples of one 16-byte vector (8 bf16, 4 floats)
+// (gemv_fits); for the QKV map, n1 and n2 must be multiples of 4 as well.  With
+// norm_w set, A's rows are RMS-normalised on the fly (A * norm_w in the
+// products, rsqrt(mean(A^2) + eps) on the accumulators); the epilogue's own
+// rscale must then be null.
 constexpr int kGemvMaxM = 4;
+template <typename T>
 bool gemv_fits(int M, int N, int K, int64_t lda);
-template <class Epi>
-hipError_t gemv_launch(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, int N, int K, const bf16* norm_w,
-                       float eps, Epi epi, hipStream_t st);
-template <class Epi>
-hipError_t gemv_dual_launch(const bf16* A, int64_t lda, const bf16* w1, const bf16* w3, int M, int N, int K,
-                            const bf16* norm_w, float eps, Epi epi, hipStream_t st);
+template <typename T, class Epi>
+hipError_t gemv_launch(const T* A, int64_t lda, WeightRows<T> w, int M, int N, int K, const T* norm_w, float eps,
+                       Epi epi, hipStream_t st);
+template <typename T, class Epi>
+hipError_t gemv_dual_launch(const T* A, int64_t lda, const T* w1, const T* w3, int M, int N, int K,
+                            const T* norm_w, float eps, Epi epi, hipStream_t st);
 
 }  // namespace llama

@@ -1,12 +1,12 @@
-// Projections at small token counts (M <= 4 rows, bf16): y[m][n] = epi(sum_k A[m][k] W[n][k]).
+// Projections at small token counts (M <= 4 rows, bf16 or fp32): y[m][n] = epi(sum_k A[m][k] W[n][k]).
 //
 // With one to four tokens every weight element is used at most four times, so
 // the projection is a stream of the weight matrix from HBM and nothing else
 // matters: no MFMA tiles, no LDS staging, no split-K partials.  A workgroup owns
 // four consecutive output columns (four weight rows, eight for the w1/w3 pair)
-// and its waves split K: of NW waves, wave w reads the 512-element chunks w, w+NW, ...,
-// each lane loading 16 bytes of every row, so one load instruction covers 1 KiB
-// of a row contiguously.  Lane partial sums are folded over the wave with
+// and its waves split K: of NW waves, wave w reads the chunks w, w+NW, ... (512
+// elements in bf16, 256 in fp32), each lane loading 16 bytes of every row, so one
+// load instruction covers 1 KiB of a row contiguously.  Lane partial sums are folded over the wave with
 // shuffles and over the waves through LDS; one thread per token row then
 // applies the fused epilogue to its four columns (the same epilogues the MFMA
 // kernels use: RoPE + cache append, SwiGLU, residual add).
@@ -23,7 +23,23 @@ namespace llama {
 namespace {
 
 constexpr int kGvCols = 4;            // output columns per workgroup
-constexpr int kGvChunk = kWave * 8;   // k elements of one 16-byte load per lane
+
+// 16-byte vectors of the element type
+template <typename T> struct GvVec;
+template <> struct GvVec<bf16> {
+  typedef bf16x8 type;
+  static constexpr int N = 8;
+  static __device__ __forceinline__ type stream(const bf16* p) { return load_stream8(p); }
+};
+template <> struct GvVec<float> {
+  typedef f32x4 type;
+  static constexpr int N = 4;
+  static __device__ __forceinline__ type stream(const float* p) {
+    return __builtin_nontemporal_load((const f32x4*)p);
+  }
+};
+template <typename T>
+constexpr int gv_chunk() { return kWave * GvVec<T>::N; }   // k elements of one 16-byte load per lane
 
 template <int M, int NR, bool NORM>
 struct GvAcc {
@@ -34,35 +50,37 @@ struct GvAcc {
 // Accumulates U chunks (c, c + NW, ...), all inside [0, nch).  Lanes past
 // the end of K (the last chunk of a ragged K) read a valid address and
 // contribute zeros.
-template <int M, int NR, bool NORM, int U, int NW>
-__device__ __forceinline__ void gv_chunks(GvAcc<M, NR, NORM>& a, const bf16* const (&wr)[NR],
-                                          const bf16* __restrict__ A, int64_t lda,
-                                          const bf16* __restrict__ norm_w, int K, int c, int lane) {
-  bf16x8 wv[U][NR];
-  bf16x8 xv[U][M];
-  bf16x8 gv[U];
+template <typename T, int M, int NR, bool NORM, int U, int NW>
+__device__ __forceinline__ void gv_chunks(GvAcc<M, NR, NORM>& a, const T* const (&wr)[NR],
+                                          const T* __restrict__ A, int64_t lda,
+                                          const T* __restrict__ norm_w, int K, int c, int lane) {
+  typedef typename GvVec<T>::type vec;
+  constexpr int EL = GvVec<T>::N;
+  vec wv[U][NR];
+  vec xv[U][M];
+  vec gv[U];
   bool ok[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    int k = (c + u * NW) * kGvChunk + lane * 8;
+    int k = (c + u * NW) * gv_chunk<T>() + lane * EL;
     ok[u] = k < K;
     k = ok[u] ? k : 0;
 #pragma unroll
-    for (int r = 0; r < NR; ++r) wv[u][r] = load_stream8(wr[r] + k);
+    for (int r = 0; r < NR; ++r) wv[u][r] = GvVec<T>::stream(wr[r] + k);
 #pragma unroll
-    for (int m = 0; m < M; ++m) xv[u][m] = *(const bf16x8*)(A + m * lda + k);
-    if constexpr (NORM) gv[u] = *(const bf16x8*)(norm_w + k);
+    for (int m = 0; m < M; ++m) xv[u][m] = *(const vec*)(A + m * lda + k);
+    if constexpr (NORM) gv[u] = *(const vec*)(norm_w + k);
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      float xf[8];
+      float xf[EL];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) xf[i] = ok[u] ? (float)xv[u][m][i] : 0.0f;
+      for (int i = 0; i < EL; ++i) xf[i] = ok[u] ? (float)xv[u][m][i] : 0.0f;
       if constexpr (NORM) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < EL; ++i) {
           a.ss[m] += xf[i] * xf[i];
           xf[i] *= (float)gv[u][i];
         }
@@ -70,21 +88,21 @@ __device__ __forceinline__ void gv_chunks(GvAcc<M, NR, NORM>& a, const bf16* con
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a.acc[m][r] += xf[i] * (float)wv[u][r][i];
+        for (int i = 0; i < EL; ++i) a.acc[m][r] += xf[i] * (float)wv[u][r][i];
       }
     }
   }
 }
 
-template <int M, int NW, bool DUAL, bool NORM, class Epi>
+template <typename T, int M, int NW, bool DUAL, bool NORM, class Epi>
 __global__ void __launch_bounds__(NW * kWave)
-gemv_bf16(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int K, const bf16* __restrict__ norm_w,
-          float eps, Epi epi) {
+gemv_kernel(const T* __restrict__ A, int64_t lda, WeightRows<T> w, int K, const T* __restrict__ norm_w,
+            float eps, Epi epi) {
   constexpr int NR = DUAL ? 2 * kGvCols : kGvCols;   // weight rows streamed
   constexpr int U = DUAL ? 1 : 2;                     // chunks in flight: 8 row loads per lane
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int n0 = blockIdx.x * kGvCols;
-  const bf16* wr[NR];
+  const T* wr[NR];
   if constexpr (DUAL) {
 #pragma unroll
     for (int r = 0; r < kGvCols; ++r) {
@@ -93,7 +111,7 @@ gemv_bf16(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int K, co
     }
   } else {
     // n1 and n2 are multiples of four: the four rows lie in one matrix
-    const bf16* base = n0 < w.n1 ? w.w0 + (int64_t)n0 * K
+    const T* base = n0 < w.n1 ? w.w0 + (int64_t)n0 * K
                                  : (n0 < w.n2 ? w.w1 + (int64_t)(n0 - w.n1) * K : w.w2 + (int64_t)(n0 - w.n2) * K);
 #pragma unroll
     for (int r = 0; r < NR; ++r) wr[r] = base + (int64_t)r * K;
@@ -106,11 +124,11 @@ gemv_bf16(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int K, co
 #pragma unroll
     for (int r = 0; r < NR; ++r) a.acc[m][r] = 0.0f;
   }
-  const int nch = (K + kGvChunk - 1) / kGvChunk;
+  const int nch = (K + gv_chunk<T>() - 1) / gv_chunk<T>();
   int c = wave;
-  for (; c + (U - 1) * NW < nch; c += U * NW) gv_chunks<M, NR, NORM, U, NW>(a, wr, A, lda, norm_w, K, c, lane);
+  for (; c + (U - 1) * NW < nch; c += U * NW) gv_chunks<T, M, NR, NORM, U, NW>(a, wr, A, lda, norm_w, K, c, lane);
   if constexpr (U > 1) {
-    for (; c < nch; c += NW) gv_chunks<M, NR, NORM, 1, NW>(a, wr, A, lda, norm_w, K, c, lane);
+    for (; c < nch; c += NW) gv_chunks<T, M, NR, NORM, 1, NW>(a, wr, A, lda, norm_w, K, c, lane);
   }
 
   __shared__ float red[NW][M][NR + 1];
@@ -145,15 +163,15 @@ gemv_bf16(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int K, co
   }
 }
 
-template <int NW, bool DUAL, bool NORM, class Epi>
-hipError_t gv_launch_nw(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, int N, int K, const bf16* norm_w,
+template <typename T, int NW, bool DUAL, bool NORM, class Epi>
+hipError_t gv_launch_nw(const T* A, int64_t lda, WeightRows<T> w, int M, int N, int K, const T* norm_w,
                         float eps, Epi epi, hipStream_t st) {
   const dim3 grid(N / kGvCols), block(NW * kWave);
   switch (M) {
-    case 1: gemv_bf16<1, NW, DUAL, NORM, Epi><<<grid, block, 0, st>>>(A, lda, w, K, norm_w, eps, epi); break;
-    case 2: gemv_bf16<2, NW, DUAL, NORM, Epi><<<grid, block, 0, st>>>(A, lda, w, K, norm_w, eps, epi); break;
-    case 3: gemv_bf16<3, NW, DUAL, NORM, Epi><<<grid, block, 0, st>>>(A, lda, w, K, norm_w, eps, epi); break;
-    case 4: gemv_bf16<4, NW, DUAL, NORM, Epi><<<grid, block, 0, st>>>(A, lda, w, K, norm_w, eps, epi); break;
+    case 1: gemv_kernel<T, 1, NW, DUAL, NORM, Epi><<<grid, block, 0, st>>>(A, lda, w, K, norm_w, eps, epi); break;
+    case 2: gemv_kernel<T, 2, NW, DUAL, NORM, Epi><<<grid, block, 0, st>>>(A, lda, w, K, norm_w, eps, epi); break;
+    case 3: gemv_kernel<T, 3, NW, DUAL, NORM, Epi><<<grid, block, 0, st>>>(A, lda, w, K, norm_w, eps, epi); break;
+    case 4: gemv_kernel<T, 4, NW, DUAL, NORM, Epi><<<grid, block, 0, st>>>(A, lda, w, K, norm_w, eps, epi); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -162,46 +180,55 @@ hipError_t gv_launch_nw(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, i
 // Four waves per workgroup, or eight when the grid is small (under 2048
 // workgroups, e.g. 4096 output columns): the extra waves keep more weight
 // loads in flight per CU.
-template <bool DUAL, bool NORM, class Epi>
-hipError_t gv_launch(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, int N, int K, const bf16* norm_w,
+template <typename T, bool DUAL, bool NORM, class Epi>
+hipError_t gv_launch(const T* A, int64_t lda, WeightRows<T> w, int M, int N, int K, const T* norm_w,
                      float eps, Epi epi, hipStream_t st) {
-  if (N / kGvCols < 2048 && K > 4 * kGvChunk)
-    return gv_launch_nw<8, DUAL, NORM>(A, lda, w, M, N, K, norm_w, eps, epi, st);
-  return gv_launch_nw<4, DUAL, NORM>(A, lda, w, M, N, K, norm_w, eps, epi, st);
+  if (N / kGvCols < 2048 && K > 4 * gv_chunk<T>())
+    return gv_launch_nw<T, 8, DUAL, NORM>(A, lda, w, M, N, K, norm_w, eps, epi, st);
+  return gv_launch_nw<T, 4, DUAL, NORM>(A, lda, w, M, N, K, norm_w, eps, epi, st);
 }
 
 }  // namespace
 
+template <typename T>
 bool gemv_fits(int M, int N, int K, int64_t lda) {
-  return M >= 1 && M <= kGemvMaxM && N > 0 && N % kGvCols == 0 && K > 0 && K % 8 == 0 && lda % 8 == 0;
+  constexpr int EL = 16 / sizeof(T);
+  return M >= 1 && M <= kGemvMaxM && N > 0 && N % kGvCols == 0 && K > 0 && K % EL == 0 && lda % EL == 0;
 }
 
-template <class Epi>
-hipError_t gemv_launch(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, int N, int K, const bf16* norm_w,
-                       float eps, Epi epi, hipStream_t st) {
-  if (!gemv_fits(M, N, K, lda) || w.n1 % kGvCols || w.n2 % kGvCols) return hipErrorInvalidValue;
-  if (norm_w) return gv_launch<false, true>(A, lda, w, M, N, K, norm_w, eps, epi, st);
-  return gv_launch<false, false>(A, lda, w, M, N, K, norm_w, eps, epi, st);
+template <typename T, class Epi>
+hipError_t gemv_launch(const T* A, int64_t lda, WeightRows<T> w, int M, int N, int K, const T* norm_w, float eps,
+                       Epi epi, hipStream_t st) {
+  if (!gemv_fits<T>(M, N, K, lda) || w.n1 % kGvCols || w.n2 % kGvCols) return hipErrorInvalidValue;
+  if (norm_w) return gv_launch<T, false, true>(A, lda, w, M, N, K, norm_w, eps, epi, st);
+  return gv_launch<T, false, false>(A, lda, w, M, N, K, norm_w, eps, epi, st);
 }
 
-template <class Epi>
-hipError_t gemv_dual_launch(const bf16* A, int64_t lda, const bf16* w1, const bf16* w3, int M, int N, int K,
-                            const bf16* norm_w, float eps, Epi epi, hipStream_t st) {
-  if (!gemv_fits(M, N, K, lda)) return hipErrorInvalidValue;
-  WeightRows<bf16> w{w1, w3, nullptr, N, N};
-  if (norm_w) return gv_launch<true, true>(A, lda, w, M, N, K, norm_w, eps, epi, st);
-  return gv_launch<true, false>(A, lda, w, M, N, K, norm_w, eps, epi, st);
+template <typename T, class Epi>
+hipError_t gemv_dual_launch(const T* A, int64_t lda, const T* w1, const T* w3, int M, int N, int K,
+                            const T* norm_w, float eps, Epi epi, hipStream_t st) {
+  if (!gemv_fits<T>(M, N, K, lda)) return hipErrorInvalidValue;
+  WeightRows<T> w{w1, w3, nullptr, N, N};
+  if (norm_w) return gv_launch<T, true, true>(A, lda, w, M, N, K, norm_w, eps, epi, st);
+  return gv_launch<T, true, false>(A, lda, w, M, N, K, norm_w, eps, epi, st);
 }
 
-template hipError_t gemv_launch<EpiStore<bf16>>(const bf16*, int64_t, WeightRows<bf16>, int, int, int, const bf16*,
-                                                float, EpiStore<bf16>, hipStream_t);
-template hipError_t gemv_launch<EpiResidual<bf16>>(const bf16*, int64_t, WeightRows<bf16>, int, int, int,
-                                                   const bf16*, float, EpiResidual<bf16>, hipStream_t);
-template hipError_t gemv_launch<EpiQKV<bf16>>(const bf16*, int64_t, WeightRows<bf16>, int, int, int, const bf16*,
-                                              float, EpiQKV<bf16>, hipStream_t);
-template hipError_t gemv_launch<EpiF32>(const bf16*, int64_t, WeightRows<bf16>, int, int, int, const bf16*, float,
-                                        EpiF32, hipStream_t);
-template hipError_t gemv_dual_launch<EpiSwiGLU<bf16>>(const bf16*, int64_t, const bf16*, const bf16*, int, int, int,
-                                                      const bf16*, float, EpiSwiGLU<bf16>, hipStream_t);
+#define LLAMA_GEMV_INST(T)                                                                                        \
+  template bool gemv_fits<T>(int, int, int, int64_t);                                                            \
+  template hipError_t gemv_launch<T, EpiStore<T>>(const T*, int64_t, WeightRows<T>, int, int, int, const T*, float, \
+                                                  EpiStore<T>, hipStream_t);                                     \
+  template hipError_t gemv_launch<T, EpiResidual<T>>(const T*, int64_t, WeightRows<T>, int, int, int, const T*,   \
+                                                     float, EpiResidual<T>, hipStream_t);                        \
+  template hipError_t gemv_launch<T, EpiQKV<T>>(const T*, int64_t, WeightRows<T>, int, int, int, const T*, float, \
+                                                EpiQKV<T>, hipStream_t);                                         \
+  template hipError_t gemv_dual_launch<T, EpiSwiGLU<T>>(const T*, int64_t, const T*, const T*, int, int, int,     \
+                                                        const T*, float, EpiSwiGLU<T>, hipStream_t);
+
+LLAMA_GEMV_INST(bf16)
+LLAMA_GEMV_INST(float)
+template hipError_t gemv_launch<bf16, EpiF32>(const bf16*, int64_t, WeightRows<bf16>, int, int, int, const bf16*,
+                                              float, EpiF32, hipStream_t);
+template hipError_t gemv_launch<float, EpiF32>(const float*, int64_t, WeightRows<float>, int, int, int, const float*,
+                                               float, EpiF32, hipStream_t);
 
 }  // namespace llama

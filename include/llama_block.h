@@ -205,10 +205,10 @@ int llama_block_forward(const llama_model_args* args, const llama_block_weights*
  * before the first kernel and events[i] after stage i, the stages being
  * 1 attention_norm, 2 QKV projection + RoPE + cache append, 3 attention,
  * 4 wo + residual, 5 ffn_norm, 6 w1/w3 + SwiGLU, 7 w2 + residual.
- * hipEventElapsedTime(events[i-1], events[i]) is stage i's duration.  In bf16,
- * calls of one to four tokens normalise inside stages 2 and 6, and calls of
- * 5 to 64 tokens whose wo projection is split over K compute ffn_norm inside
- * stage 4: the normalisation stages then hold no kernel. */
+ * hipEventElapsedTime(events[i-1], events[i]) is stage i's duration.  Calls of
+ * one to four tokens normalise inside stages 2 and 6, and bf16 calls of 5 to 64
+ * tokens whose wo projection is split over K compute ffn_norm inside stage 4:
+ * the normalisation stages then hold no kernel. */
 int llama_block_forward_events(const llama_model_args* args, const llama_block_weights* weights,
                                void* cache_k, void* cache_v, const float* freqs_cis,
                                int32_t freqs_end, const void* x, void* out, int32_t bsz,

@@ -98,6 +98,8 @@ def test_rope_apply(dtype):
     ("bf16", 3, 40, 100),         # K below one chunk: most lanes idle
     ("bf16", 4, 8, 4),            # one lane of one wave holds all of K; a single workgroup
     ("f32", 70, 260, 132),
+    ("f32", 1, 260, 132),         # fp32 weight stream: K = 256 + 4 (a ragged 256-element chunk)
+    ("f32", 4, 1024, 64),         # four tokens, four chunks of 256
 ])
 def test_linear(dtype, M, K, N):
     need_gpu()
@@ -135,7 +137,9 @@ def _linear_case(dtype, M, K, N):
     ("bf16", 7, 352, 1024),
     # one to four tokens: weight-streaming kernels (dim = 512 is one chunk: three waves idle;
     # 640 = 512 + 128 and 1712 = 3 * 512 + 176 end in ragged chunks)
-    ("bf16", 1, 512, 1536), ("bf16", 4, 640, 1712), ("bf16", 2, 4096, 14336)])
+    ("bf16", 1, 512, 1536), ("bf16", 4, 640, 1712), ("bf16", 2, 4096, 14336),
+    # fp32 weight streams
+    ("f32", 1, 256, 768), ("f32", 3, 260, 772)])
 def test_swiglu_ffn(dtype, rows, dim, hidden):
     need_gpu()
     _swiglu_case(dtype, rows, dim, hidden)
