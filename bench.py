@@ -357,6 +357,27 @@ def bench_stack(dev, steps):
     dec_g = e[0].elapsed_time(e[1]) / steps
     log(f"stack decode from a HIP graph {dec_g:.3f} ms/step")
     del graph
+    # the same loop sampling with temperature 0.8 and top-p 0.95 (the walkthrough's
+    # defaults); fresh uniforms are copied in between replays, as generate() does
+    pos.fill_(w.prefill_len)
+    tok.copy_(out[0])
+    gu = torch.Generator(device=dev).manual_seed(7)
+    us = torch.rand(steps + 1, w.batch, generator=gu, device=dev)
+    ubuf = us[0].clone()
+    stack.decode_step_at(tok, pos, max_pos, logits, 0.8, 0.95, ubuf)      # eager first step
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        stack.decode_step_at(tok, pos, max_pos, logits, 0.8, 0.95, ubuf)
+    torch.cuda.synchronize()
+    e[0].record()
+    for t in range(steps):
+        ubuf.copy_(us[t + 1])
+        graph.replay()
+    e[1].record()
+    torch.cuda.synchronize()
+    dec_s = e[0].elapsed_time(e[1]) / steps
+    log(f"stack sampled decode from a HIP graph {dec_s:.3f} ms/step")
+    del graph
     # top-p sampling of the last step's logits (temperature 0.8, top_p 0.95: the walkthrough's defaults)
     g = torch.Generator(device=dev).manual_seed(5)
     uni = torch.rand(20, w.batch, generator=g, device=dev)
@@ -373,6 +394,8 @@ def bench_stack(dev, steps):
     res = {"prefill_ms": round(pre, 2), "prefill_tokens_per_s": round(w.batch * w.prefill_len / pre * 1e3, 1),
            "decode_ms_per_step": round(dec, 3), "decode_tokens_per_s": round(w.batch / dec * 1e3, 1),
            "graph_decode_ms_per_step": round(dec_g, 3), "graph_decode_tokens_per_s": round(w.batch / dec_g * 1e3, 1),
+           "graph_sampled_decode_ms_per_step": round(dec_s, 3),
+           "graph_sampled_decode_tokens_per_s": round(w.batch / dec_s * 1e3, 1),
            "decode_steps_timed": steps, "batch": w.batch, "prompt": w.prefill_len, "layers": w.n_layers,
            "top_p_sampling_us": round(samp * 1e3, 1)}
     del stack
