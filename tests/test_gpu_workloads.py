@@ -219,6 +219,10 @@ RAGGED4 = wl.Workload(32, "ragged-640-b4", "bf16", 640, 5, 1, 1712, 8, None, 1e-
 # wo's split reduction fused with the residual add and ffn_norm
 SMALL_ROWS6 = wl.Workload(34, "small-gqa-8kv-b6", "bf16", 2048, 16, 8, 1536, 256, 0.25, 1e-5, 5e5, batch=6,
                           prefill_len=100, decode_steps=4)
+# 16 sequences x 8 kv heads = 128 units: decode attention runs one 8-wave workgroup per
+# unit (no split), also with the position read from device memory
+SMALL_ROWS16 = wl.Workload(35, "small-gqa-8kv-b16", "bf16", 2048, 16, 8, 1536, 256, 0.25, 1e-5, 5e5, batch=16,
+                           prefill_len=100, decode_steps=4)
 RAGGED1 = wl.Workload(33, "ragged-640-b1", "bf16", 640, 5, 1, 1712, 8, None, 1e-5, 1e4, batch=1, prefill_len=45,
                       decode_steps=4)
 
@@ -272,7 +276,7 @@ def test_determinism_batch_independence_causality():
 
 
 @pytest.mark.parametrize("max_pos", [4000, 1000, 137])
-@pytest.mark.parametrize("w", [SMALL, SMALL_ROWS], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [SMALL, SMALL_ROWS, SMALL_ROWS16], ids=lambda w: w.name)
 def test_decode_at_device_position_matches_oracle(w, max_pos):
     """llama_block_decode_at reads the position from device memory.  With a bound
     above the actual position (max_start_pos 4000, 1000 or 137 while the steps run at
