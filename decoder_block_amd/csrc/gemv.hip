@@ -4,18 +4,19 @@
 // the projection is a stream of the weight matrix from HBM and nothing else
 // matters: no MFMA tiles, no LDS staging, no split-K partials.  A workgroup owns
 // four consecutive output columns (four weight rows, eight for the w1/w3 pair)
-// and its waves split K: of NW waves, wave w reads the chunks w, w+NW, ... (512
-// elements in bf16, 256 in fp32), each lane loading 16 bytes of every row, so one
-// load instruction covers 1 KiB of a row contiguously.  Lane partial sums are folded over the wave with
-// shuffles and over the waves through LDS; one thread per token row then
-// applies the fused epilogue to its four columns (the same epilogues the MFMA
-// kernels use: RoPE + cache append, SwiGLU, residual add).
+// and its waves split K: of NW waves, wave w reads the chunks w, w+NW, ...
+// (512 elements in bf16, 256 in fp32), each lane loading 16 bytes of every row,
+// so one load instruction covers 1 KiB of a row contiguously.  Lane partial
+// sums are folded over the wave with shuffles and over the waves through LDS;
+// one thread per token row then applies the fused epilogue to its four columns
+// (the same epilogues the MFMA kernels use: RoPE + cache append, SwiGLU,
+// residual add).
 //
 // With norm_w set, A is the un-normalised block input and the kernel applies
-// RMSNorm on the fly (LLaMA's RMSNorm module): the products use A * norm_w and
-// the row factor rsqrt(mean(A^2) + eps) scales the fp32 accumulators, with the
-// sum of squares taken from the same A loads.  The decode step then needs no
-// separate normalisation pass.
+// RMSNorm on the fly (LLaMA notes, section 3, class RMSNorm): the products use
+// A * norm_w and the row factor rsqrt(mean(A^2) + eps) scales the fp32
+// accumulators, with the sum of squares taken from the same A loads.  The
+// decode step then needs no separate normalisation pass.
 #include "gemm.hpp"
 
 namespace llama {
