@@ -26,11 +26,17 @@ constexpr int kBigStages = 2;
 constexpr int kBigWaves = 8;
 constexpr int kCUs = 256;         // MI355X compute units
 // small M (<= 64 tokens: the weights stream from HBM once): 64-deep k-tiles
-// (128-byte row pieces).  Tiles: M <= 32: 32 rows x 128 columns in a 6-stage
-// ring, 32 x 256 for the dual w1/w3 kernel (4 stages); 33..64 rows: 64 x 128,
-// 6 stages.  Narrow tiles need fewer K-splits to cover the CUs (measured:
-// LLaMA-3-8B-shaped w1/w3 at M = 64 went from 70 to 48 us).
+// (128-byte row pieces).  Tiles: M <= 32: 32 rows x 128 columns, 32 x 256 for
+// the dual w1/w3 kernel; 33..64 rows: 64 x 128.  Narrow tiles need fewer
+// K-splits to cover the CUs (measured: LLaMA-3-8B-shaped w1/w3 at M = 64 went
+// from 70 to 48 us).  Ring depths: more stages buy no weight bandwidth here
+// (the DMA queue is already deep), while a smaller LDS footprint lets the next
+// kernel's workgroups start on a CU before the last ones of this kernel end --
+// measured over whole decode steps, 3 stages for the plain 64-row tile and 4
+// for the others ran 1-2% faster than 6.
 constexpr int kSkinnyBK = 64;
+constexpr int kSkinnyStages = 4;         // 32 x 128, dual 32 x 256, dual 64 x 128
+constexpr int kSkinnyStages64 = 3;       // 64 x 128
 // cache-policy operand of the LDS-DMA load: the non-temporal bit (gfx940 family)
 constexpr int kCpolNT = 2;
 
@@ -689,11 +695,18 @@ hipError_t launch_bf16(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, in
   if (lda % 8 == 0 && M <= 64 && K % kSkinnyBK == 0) {
     if (M <= 32) {
       if constexpr (DUAL)
-        return launch_dma<32, 256, kSkinnyBK, 1, 4, DUAL, 4>(A, lda, w, M, N, K, epi, splits, partial, st);
+        return launch_dma<32, 256, kSkinnyBK, 1, kSkinnyStages, DUAL, 4>(A, lda, w, M, N, K, epi, splits,
+                                                                           partial, st);
       else
-        return launch_dma<32, 128, kSkinnyBK, 1, 6, DUAL, 4>(A, lda, w, M, N, K, epi, splits, partial, st);
+        return launch_dma<32, 128, kSkinnyBK, 1, kSkinnyStages, DUAL, 4>(A, lda, w, M, N, K, epi, splits,
+                                                                           partial, st);
     }
-    return launch_dma<64, 128, kSkinnyBK, 2, 6, DUAL, 4>(A, lda, w, M, N, K, epi, splits, partial, st);
+    if constexpr (DUAL)
+      return launch_dma<64, 128, kSkinnyBK, 2, kSkinnyStages, DUAL, 4>(A, lda, w, M, N, K, epi, splits,
+                                                                       partial, st);
+    else
+      return launch_dma<64, 128, kSkinnyBK, 2, kSkinnyStages64, DUAL, 4>(A, lda, w, M, N, K, epi, splits,
+                                                                         partial, st);
   }
   if (lda % 8 == 0 && M > 64 && K % kBigBK == 0)
     return launch_dma<256, 256, kBigBK, 2, kBigStages, DUAL, kBigWaves>(A, lda, w, M, N, K, epi, splits, partial,
@@ -749,10 +762,10 @@ hipError_t gemm_residual_norm_launch(const bf16* A, int64_t lda, const bf16* w, 
   if ((int64_t)(splits - 1) * kps >= K) return hipErrorInvalidValue;
   dim3 grid(tiles, 1, splits);
   if (M <= 32)
-    gemm_bf16_dma<32, 128, kSkinnyBK, 1, 6, false, true, EpiResidual<bf16>, 4>
+    gemm_bf16_dma<32, 128, kSkinnyBK, 1, kSkinnyStages, false, true, EpiResidual<bf16>, 4>
         <<<grid, 256, 0, st>>>(A, lda, wr, M, N, K, kps, epi, partial);
   else
-    gemm_bf16_dma<64, 128, kSkinnyBK, 2, 6, false, true, EpiResidual<bf16>, 4>
+    gemm_bf16_dma<64, 128, kSkinnyBK, 2, kSkinnyStages64, false, true, EpiResidual<bf16>, 4>
         <<<grid, 256, 0, st>>>(A, lda, wr, M, N, K, kps, epi, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -780,12 +793,12 @@ int gemm_pick_splits(int M, int N, int K, bool dual, bool is_bf16) {
   // small token count: the weights stream from HBM once; split K so that the
   // grid covers the CUs
   if (is_bf16 && K % kSkinnyBK == 0) {
-    // LDS-DMA kernel: its ring fills most of a CU's LDS, so one workgroup per CU;
-    // aim at one wave of workgroups (fewer splits measured faster than
-    // oversubscribing: every split adds an fp32 partial tile and shortens the
-    // pipeline), each split keeping at least a ring's depth of k-tiles
+    // LDS-DMA kernel: aim at one workgroup per CU (fewer splits measured faster
+    // than oversubscribing, also with rings small enough for two per CU: every
+    // split adds an fp32 partial tile and shortens the pipeline), each split
+    // keeping at least a ring's depth of k-tiles
     const int bn_out = dual ? (M <= 32 ? 128 : 64) : 128;
-    const int stages = (dual && M <= 32) ? 4 : 6;
+    const int stages = (M <= 32 || dual) ? kSkinnyStages : kSkinnyStages64;
     const int tiles = (N + bn_out - 1) / bn_out;
     const int nkt = K / kSkinnyBK;
     int s = tiles >= kCUs ? 1 : kCUs / tiles;
