@@ -225,6 +225,9 @@ SMALL_ROWS16 = wl.Workload(35, "small-gqa-8kv-b16", "bf16", 2048, 16, 8, 1536, 2
                            prefill_len=100, decode_steps=4)
 RAGGED1 = wl.Workload(33, "ragged-640-b1", "bf16", 640, 5, 1, 1712, 8, None, 1e-5, 1e4, batch=1, prefill_len=45,
                       decode_steps=4)
+# 40 tokens per decode step: 64-row tiles over 40 rows (a ragged row tail) with K split
+SMALL_ROWS40 = wl.Workload(36, "small-gqa-8kv-b40", "bf16", 2048, 16, 8, 1536, 256, 0.25, 1e-5, 5e5, batch=40,
+                           prefill_len=100, decode_steps=3)
 
 
 def _small_runner(dev, batch=None, w=SMALL):
@@ -254,6 +257,41 @@ def test_decode_chain_matches_prefill_and_oracle(w):
     check(chain, ref, "bf16", "small prefill + decode chain")
     check(chunked, ref, "bf16", "small chunked prefill")
     check(chain, f64(full), "bf16", "chain vs full prefill (GPU vs GPU)")
+
+
+@pytest.mark.parametrize("w", [SMALL_ROWS6, SMALL_ROWS16, SMALL_ROWS40], ids=lambda w: w.name)
+def test_decode_step_ignores_workspace_contents(w):
+    """5-64 tokens: the projections split K through fp32 partial tiles in the
+    workspace (wo's reduction fused with ffn_norm).  Each decode step runs three
+    times: over a workspace with every bit set, over a zeroed one, and over the
+    previous call's leftovers; the outputs must agree bit for bit and follow the
+    oracle's prefill + decode chain (40 rows: 64-row tiles with a ragged tail)."""
+    dev = need_gpu()
+    print(f"case {w.name}: decode steps over filled, zeroed and reused workspaces", flush=True)
+    x = wl.activations(w).to(dev)
+    a = w.prefill_len
+    r = _small_runner(dev, w=w)
+    parts = [r.forward(x[:, :a].contiguous(), 0)]
+    for t in range(w.decode_steps):
+        xt = x[:, a + t:a + t + 1].contiguous()
+        r.reserve(w.batch, 1, a + t)
+        r.ws.fill_(255)
+        o1 = r.forward(xt, a + t).clone()
+        r.ws.zero_()
+        o2 = r.forward(xt, a + t).clone()
+        o3 = r.forward(xt, a + t).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2), f"step {t}: a workspace with every bit set changed the output"
+        assert torch.equal(o2, o3), f"step {t}: the previous call's workspace contents changed the output"
+        parts.append(o1)
+    chain = torch.cat(parts, dim=1)
+    n = a + w.decode_steps
+    shape = (w.batch, w.max_seq_len, w.n_kv_heads, w.head_dim)
+    ck, cv = np.zeros(shape), np.zeros(shape)
+    ref = ob.block_forward(f64(x[:, :n]), _w64(wl.block_weights(w)), ck, cv, 0, w.n_heads, w.n_kv_heads,
+                           w.norm_eps, w.rope_theta)
+    check(chain, ref, "bf16", "prefill + decode chain")
+    check(r.cache_k[:, :n], ck[:, :n], "bf16", "cache_k rows")
 
 
 def test_determinism_batch_independence_causality():
