@@ -551,8 +551,7 @@ gemm_f32_fma(const float* __restrict__ A, int64_t lda, WeightRows<float> w, int 
 // ------------------------------------------------------------------ split-K reduce
 // Z lanes share one output group (4 columns of one row): lane z sums the splits
 // z, z+Z, ... (independent loads in flight), xor-shuffles combine the Z partial
-// sums and lane 0 applies the epilogue.  Z = 8 when there are few groups (one
-// token: the latency of the split walk dominates), 1 otherwise.
+// sums and lane 0 applies the epilogue (Z chosen by launch_reduce).
 template <bool DUAL, int Z, class Epi>
 __global__ void __launch_bounds__(kThreads)
 splitk_reduce(const float* __restrict__ partial, int splits, int M, int N, Epi epi) {
@@ -637,11 +636,16 @@ reduce_residual_norm(const float* __restrict__ partial, int splits, int M, int N
 template <bool DUAL, class Epi>
 hipError_t launch_reduce(const float* partial, int splits, int M, int N, Epi epi, hipStream_t st) {
   const int64_t groups = (int64_t)M * (N / 4);
-  // eight lanes per group when the groups are few or the splits many (more than
-  // one batch of loads per lane would serialise the walk)
-  if (groups < 32768 || splits > 4) {
+  // lanes per group: eight when the groups are few (one token: the latency of
+  // the split walk dominates), two for decode-sized outputs (measured over whole
+  // 32-layer batch-64 decode steps: 6.61 ms with eight, 6.55 with one or four,
+  // 6.48 with two), one for prefill-sized outputs, which run at HBM speed
+  if (groups < 32768) {
     const int blocks = (int)((groups * 8 + kThreads - 1) / kThreads);
     splitk_reduce<DUAL, 8, Epi><<<blocks, kThreads, 0, st>>>(partial, splits, M, N, epi);
+  } else if (groups < (1 << 20)) {
+    const int blocks = (int)((groups * 2 + kThreads - 1) / kThreads);
+    splitk_reduce<DUAL, 2, Epi><<<blocks, kThreads, 0, st>>>(partial, splits, M, N, epi);
   } else {
     const int blocks = (int)((groups + kThreads - 1) / kThreads);
     splitk_reduce<DUAL, 1, Epi><<<blocks < 16384 ? blocks : 16384, kThreads, 0, st>>>(partial, splits, M, N, epi);
