@@ -39,13 +39,16 @@ rmsnorm_kernel(const T* __restrict__ x, int64_t x_stride, const T* __restrict__ 
   const T* xr = x + row * x_stride;
   T* yr = y + row * (int64_t)dim;
   const int nvec = dim / V;
-  vec cached[CACHE];
+  // the row's first CACHE * kThreads vectors and their gains are loaded up front
+  // (the gain loads would otherwise wait behind the reduction)
+  vec cached[CACHE], wcached[CACHE];
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < CACHE; ++c) {
     int i = threadIdx.x + c * kThreads;
     if (i < nvec) {
       cached[c] = *(const vec*)(xr + i * V);
+      wcached[c] = *(const vec*)(w + i * V);
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         float f = (float)cached[c][e];
@@ -70,8 +73,7 @@ rmsnorm_kernel(const T* __restrict__ x, int64_t x_stride, const T* __restrict__ 
   const float rr = 1.0f / sqrtf(tot / (float)dim + eps);
   const float r = rscale ? 1.0f : rr;
   if (rscale && threadIdx.x == 0) rscale[row] = rr;
-  auto emit = [&](int i, const vec& v) {
-    vec wv = *(const vec*)(w + i * V);
+  auto emit = [&](int i, const vec& v, const vec& wv) {
     vec o;
 #pragma unroll
     for (int e = 0; e < V; ++e) o[e] = from_f<T>((float)v[e] * r * (float)wv[e]);
@@ -80,9 +82,10 @@ rmsnorm_kernel(const T* __restrict__ x, int64_t x_stride, const T* __restrict__ 
 #pragma unroll
   for (int c = 0; c < CACHE; ++c) {
     int i = threadIdx.x + c * kThreads;
-    if (i < nvec) emit(i, cached[c]);
+    if (i < nvec) emit(i, cached[c], wcached[c]);
   }
-  for (int i = threadIdx.x + CACHE * kThreads; i < nvec; i += kThreads) emit(i, *(const vec*)(xr + i * V));
+  for (int i = threadIdx.x + CACHE * kThreads; i < nvec; i += kThreads)
+    emit(i, *(const vec*)(xr + i * V), *(const vec*)(w + i * V));
 }
 
 // RoPE table: angle p * theta^(-2i/d) and its cos/sin in fp64, stored as fp32
