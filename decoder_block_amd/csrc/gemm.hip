@@ -403,9 +403,15 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     issue(kt + NS);
+    // Large tiles: the waves leaving the barrier take issue priority while they
+    // read the new tile's first fragments and run the MFMAs that cover those
+    // reads, so the matrix pipe restarts before the other wave of the SIMD
+    // competes (measured +0.9 % on the 7B-shaped block prefill, +0.2 % on 8B).
+    if constexpr (BM > 64) __builtin_amdgcn_s_setprio(1);
     read_half((kt + 1) % NS, 0, fa[KS & 1], fb[KS & 1]);
     mfma_half(fa[(KS - 1) & 1], fb[(KS - 1) & 1]);
     interleave();
+    if constexpr (BM > 64) __builtin_amdgcn_s_setprio(0);
   }
 #pragma unroll
   for (int ks = 0; ks < KS - 1; ++ks) {
