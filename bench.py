@@ -403,6 +403,62 @@ def bench_stack(dev, steps):
     return res
 
 
+def bench_tp_share(dev, flush, reps):
+    """One GPU's share of the 70B-shaped batch-32 decode step under 8-way tensor
+    parallelism (heads split by kv head, FFN columns by eighths), at its real
+    shapes: decode attention over one kv head and its 8 query heads (32 x 4097
+    cached positions), and the SwiGLU FFN with 3584 hidden columns.  These two
+    carry 87 % of the share's bytes; the QKV and wo shares (21 and 17 MB) and the
+    two all-reduces per block are not timed here.  Each rep follows a MALL flush."""
+    import torch
+    from decoder_block_amd import _lib as L
+    g = torch.Generator(device=dev)
+    g.manual_seed(4)
+    B, T, H, Hkv, d, D, F = 32, 4097, 8, 1, 128, 8192, 3584
+    args = L.ModelArgs(dim=H * d, n_layers=1, n_heads=H, n_kv_heads=Hkv, vocab_size=-1, multiple_of=256,
+                       ffn_dim_multiplier=None, norm_eps=1e-5, rope_theta=5e5, max_batch_size=B, max_seq_len=T)
+    ck = torch.randn(B, T, Hkv, d, generator=g, device=dev).to(torch.bfloat16)
+    cv = torch.randn(B, T, Hkv, d, generator=g, device=dev).to(torch.bfloat16)
+    q = torch.randn(B, 1, H, d, generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn(B, 1, Hkv, d, generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn(B, 1, Hkv, d, generator=g, device=dev).to(torch.bfloat16)
+    o = torch.empty(B, 1, H * d, dtype=torch.bfloat16, device=dev)
+    nba = L.llama_attn_decode_workspace_size(args, B, T - 1)
+    wsa = torch.empty(max(nba, 256), dtype=torch.uint8, device=dev)
+    x = torch.randn(B, D, generator=g, device=dev).to(torch.bfloat16)
+    w1, w3 = ((torch.randn(F, D, generator=g, device=dev) * 0.02).to(torch.bfloat16) for _ in range(2))
+    w2 = (torch.randn(D, F, generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    y = torch.empty(B, D, dtype=torch.bfloat16, device=dev)
+    nbf = L.llama_ffn_workspace_size(B, D, F, L.LLAMA_BF16)
+    wsf = torch.empty(max(nbf, 256), dtype=torch.uint8, device=dev)
+    calls = {
+        "attention": (lambda: L.llama_gqa_attn_decode(q, k, v, ck, cv, o, args, B, T - 1, wsa, nba),
+                      2 * B * T * Hkv * d * 2),
+        "ffn": (lambda: L.llama_swiglu_ffn(x, w1, w3, w2, y, B, D, F, wsf, nbf), 3 * F * D * 2),
+    }
+    res = {}
+    for name, (call, nbytes) in calls.items():
+        call()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(reps):
+            flush_mall(flush)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1))
+        med = sorted(t)[len(t) // 2]
+        gbs = nbytes / (med * 1e-3) / 1e9
+        res[name] = {"us_median": round(med * 1e3, 2), "us_p10": round(pct(t, 0.1) * 1e3, 2),
+                     "us_p90": round(pct(t, 0.9) * 1e3, 2), "mbytes": round(nbytes / 1e6, 1),
+                     "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    res["shapes"] = {"batch": B, "positions": T, "q_heads": H, "kv_heads": Hkv, "head_dim": d, "dim": D,
+                     "ffn_hidden": F}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -529,7 +585,11 @@ def main():
                 "step_gbs": round((wb4 + kvb4) / (sum(tot4) / n4 * 1e-3) / 1e9, 1),
                 "step_hbm_frac": round((wb4 + kvb4) / (sum(tot4) / n4 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                 "stage_us": {n: round(v * 1e3, 2) for n, v in zip(STAGES, st4)}}
-        del r4, flush
+        del r4
+        torch.cuda.empty_cache()
+        log("workload llama2-70b decode, one GPU's share under 8-way tensor parallelism")
+        dec4["tp8_share"] = bench_tp_share(dev, flush, max(a.decode_steps, 3))
+        del flush
         torch.cuda.empty_cache()
         if not a.no_cpu_baseline:
             import numpy as np

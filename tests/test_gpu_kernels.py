@@ -97,6 +97,9 @@ def test_rope_apply(dtype):
     ("bf16", 4, 14336, 512),      # four tokens, 28 chunks (two in flight per wave, one left over)
     ("bf16", 3, 40, 100),         # K below one chunk: most lanes idle
     ("bf16", 4, 8, 4),            # one lane of one wave holds all of K; a single workgroup
+    # 70B-shaped batch-32 decode, one GPU's share under 8-way tensor parallelism: QKV (one kv head,
+    # its 8 query heads: 1280 columns) and wo (1024 input features)
+    ("bf16", 32, 8192, 1280), ("bf16", 32, 1024, 8192),
     ("f32", 70, 260, 132),
     ("f32", 1, 260, 132),         # fp32 weight stream: K = 256 + 4 (a ragged 256-element chunk)
     ("f32", 4, 1024, 64),         # four tokens, four chunks of 256
@@ -139,7 +142,9 @@ def _linear_case(dtype, M, K, N):
     # 640 = 512 + 128 and 1712 = 3 * 512 + 176 end in ragged chunks)
     ("bf16", 1, 512, 1536), ("bf16", 4, 640, 1712), ("bf16", 2, 4096, 14336),
     # fp32 weight streams
-    ("f32", 1, 256, 768), ("f32", 3, 260, 772)])
+    ("f32", 1, 256, 768), ("f32", 3, 260, 772),
+    # 70B-shaped batch-32 decode, one GPU's share of the FFN under 8-way tensor parallelism
+    ("bf16", 32, 8192, 3584)])
 def test_swiglu_ffn(dtype, rows, dim, hidden):
     need_gpu()
     _swiglu_case(dtype, rows, dim, hidden)
@@ -247,6 +252,7 @@ def test_attn_prefill_sequences_in_cache_sized_groups():
     ("bf16", 2, 300, 8, 2, 64),      # three splits, head_dim 64 (one-wave merge)
     ("bf16", 16, 1500, 16, 8, 128),  # 128 (sequence, kv head) units: one 8-wave workgroup each, no split
     ("bf16", 64, 700, 8, 4, 64),     # 256 units, head_dim 64, 8 waves
+    ("bf16", 32, 4096, 8, 1, 128),   # 70B shape at batch 32, one GPU's share under 8-way TP: 1 kv head, n_rep 8
     ("f32", 2, 79, 8, 2, 32),
 ])
 def test_attn_decode(dtype, B, p0, H, Hkv, d):
@@ -289,7 +295,7 @@ def _attn_decode_case(dtype, B, p0, H, Hkv, d):
     gck, gcv = dev(ck), dev(cv)
     out = torch.empty(B, 1, H * d, dtype=tdt(dtype), device="cuda:0")
     nbytes = dba.llama_attn_decode_workspace_size(args, B, p0)
-    # a workspace full of junk: the call must clear its split counters itself
+    # a workspace full of junk: the split partials overwrite it, nothing may read it first
     ws = torch.full((max(nbytes, 1),), 0xA5, dtype=torch.uint8, device="cuda:0")
     dba.llama_gqa_attn_decode(dev(q), dev(k), dev(v), gck, gcv, out, args, B, p0, ws, nbytes)
     torch.cuda.synchronize()
