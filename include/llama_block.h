@@ -181,7 +181,9 @@ int llama_swiglu_ffn(const void* x, const void* w1, const void* w3, const void* 
 
 /* Plain projection y = x W^T (nn.Linear without bias).  x: device [rows][in];
  * w: device [out][in]; y: device [rows][out].  Requires in % 8 == 0 and
- * out % 4 == 0 for bf16 (in, out % 4 == 0 for f32). */
+ * out % 4 == 0 for bf16 (in, out % 4 == 0 for f32).  Takes no workspace, so K
+ * is never split: for 5..64 rows and few output columns the grid is small
+ * (the block calls split those projections through their workspace). */
 int llama_linear(const void* x, const void* w, void* y, int64_t rows, int32_t in_features,
                  int32_t out_features, llama_dtype dtype, llama_stream_t stream);
 
