@@ -87,18 +87,42 @@ __global__ void __launch_bounds__(256) attn_simple(const T* __restrict__ q, cons
   const T* kb = ck + ((int64_t)b * sh.max_seq * sh.n_kv_heads + j) * HD;
   const T* vb = cv + ((int64_t)b * sh.max_seq * sh.n_kv_heads + j) * HD;
   const int kend = sh.start_pos + s + 1;
+  // Keys in blocks of U: the block's K and V rows are all loaded before any is
+  // used (a key at a time would wait out one memory latency per key), the U
+  // scores are reduced over the wave independently, and the running (max, sum,
+  // o) moves once per block.  Keys past the end are clamped for the loads and
+  // weigh 0.
+  constexpr int U = 8;
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int t = 0; t < kend; ++t) {
-    const T* kr = kb + (int64_t)t * stride;
-    float part = (has0 ? q0 * to_f(kr[lane]) : 0.f) + (has1 ? q1 * to_f(kr[lane + 64]) : 0.f);
-    float sc = wave_sum(part) * scale;
-    float mn = fmaxf(m, sc);
-    float a = expf(m - mn), p = expf(sc - mn);
-    const T* vr = vb + (int64_t)t * stride;
-    l = l * a + p;
-    o0 = o0 * a + (has0 ? p * to_f(vr[lane]) : 0.f);
-    o1 = o1 * a + (has1 ? p * to_f(vr[lane + 64]) : 0.f);
-    m = mn;
+  for (int t0 = 0; t0 < kend; t0 += U) {
+    float k0[U], k1[U], v0[U], v1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t off = (int64_t)min(t0 + u, kend - 1) * stride;
+      k0[u] = has0 ? to_f(kb[off + lane]) : 0.f;
+      k1[u] = has1 ? to_f(kb[off + lane + 64]) : 0.f;
+      v0[u] = has0 ? to_f(vb[off + lane]) : 0.f;
+      v1[u] = has1 ? to_f(vb[off + lane + 64]) : 0.f;
+    }
+    float sc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) sc[u] = wave_sum(q0 * k0[u] + q1 * k1[u]) * scale;
+    float mb = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (t0 + u < kend) mb = fmaxf(mb, sc[u]);
+    const float a = expf(m - mb);             // 0 on the first block (m = -inf)
+    l *= a;
+    o0 *= a;
+    o1 *= a;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float p = t0 + u < kend ? expf(sc[u] - mb) : 0.f;
+      l += p;
+      o0 += p * v0[u];
+      o1 += p * v1[u];
+    }
+    m = mb;
   }
   T* orow = out + bs * (int64_t)H * HD + (int64_t)h * HD;
   if (has0) orow[lane] = from_f<T>(o0 / l);

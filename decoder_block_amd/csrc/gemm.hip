@@ -497,21 +497,37 @@ gemm_f32_fma(const float* __restrict__ A, int64_t lda, WeightRows<float> w, int 
   const int kb = blockIdx.z * k_per_split, ke = min(K, kb + k_per_split);
   const int tx = tid % 16, ty = tid / 16;  // n block tx*4, m block ty*4
   float acc[DUAL ? 2 : 1][4][4] = {};
-  for (int k0 = kb; k0 < ke; k0 += BK) {
-    // each thread loads 4 elements of A and 4 (x2) of W
-    for (int e = tid; e < BM * BK; e += kThreads) {
-      int r = e / BK, c = e % BK;
-      int m = m0 + r, k = k0 + c;
-      As[c][r] = (m < M && k < ke) ? A[(int64_t)m * lda + k] : 0.f;
-      int n = n0 + r;
+  // each thread stages 4 elements of A and 4 (x2) of W per k-tile; the next
+  // tile's global loads are issued into registers before the current tile's
+  // products, so their latency overlaps the arithmetic
+  constexpr int EPT = BM * BK / kThreads;
+  static_assert(EPT * kThreads == BM * BK && BM == BN, "staging");
+  float ra[EPT], rw[DUAL ? 2 : 1][EPT];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int e = tid + i * kThreads, r = e / BK, c = e % BK;
+      const int m = m0 + r, n = n0 + r, k = k0 + c;
+      ra[i] = (m < M && k < ke) ? A[(int64_t)m * lda + k] : 0.f;
       if (DUAL) {
-        Ws[0][c][r] = (n < N && k < ke) ? w.w0[(int64_t)n * K + k] : 0.f;
-        Ws[DUAL ? 1 : 0][c][r] = (n < N && k < ke) ? w.w1[(int64_t)n * K + k] : 0.f;
+        rw[0][i] = (n < N && k < ke) ? w.w0[(int64_t)n * K + k] : 0.f;
+        rw[DUAL ? 1 : 0][i] = (n < N && k < ke) ? w.w1[(int64_t)n * K + k] : 0.f;
       } else {
-        Ws[0][c][r] = (n < N && k < ke) ? weight_row(w, n, K)[k] : 0.f;
+        rw[0][i] = (n < N && k < ke) ? weight_row(w, n, K)[k] : 0.f;
       }
     }
+  };
+  if (kb < ke) gload(kb);
+  for (int k0 = kb; k0 < ke; k0 += BK) {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int e = tid + i * kThreads, r = e / BK, c = e % BK;
+      As[c][r] = ra[i];
+#pragma unroll
+      for (int d = 0; d < (DUAL ? 2 : 1); ++d) Ws[d][c][r] = rw[d][i];
+    }
     __syncthreads();
+    if (k0 + BK < ke) gload(k0 + BK);
 #pragma unroll
     for (int c = 0; c < BK; ++c) {
       float a[4], b[DUAL ? 2 : 1][4];
