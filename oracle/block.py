@@ -178,16 +178,6 @@ def linear(x: np.ndarray, w: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------- block
-def qkv(xn: np.ndarray, wq, wk, wv, n_heads: int, n_kv_heads: int):
-    """q, k, v projections viewed per head (same notes, section 3, Attention.forward)."""
-    B, S, D = xn.shape
-    d = D // n_heads
-    q = linear(xn, wq).reshape(B, S, n_heads, d)
-    k = linear(xn, wk).reshape(B, S, n_kv_heads, d)
-    v = linear(xn, wv).reshape(B, S, n_kv_heads, d)
-    return q, k, v
-
-
 def block_forward(x: np.ndarray, w: Dict[str, np.ndarray], cache_k: np.ndarray, cache_v: np.ndarray,
                   start_pos: int, n_heads: int, n_kv_heads: int, norm_eps: float, rope_theta: float,
                   rows: Optional[Sequence[int]] = None, trace: Optional[dict] = None) -> np.ndarray:
