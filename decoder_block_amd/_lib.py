@@ -225,13 +225,54 @@ def llama_linear(x, w, y, rows: int, in_features: int, out_features: int, stream
                               _stream(stream)), "llama_linear")
 
 
+BLOCK_TENSORS = ("attention_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w1", "w2", "w3")
+
+
+def block_tensor_shapes(args: ModelArgs) -> dict:
+    """The [out, in] (or [dim]) shape of each block parameter that ``args`` implies."""
+    D, H = args.dim, args.n_heads
+    Hkv = args.n_kv_heads or H
+    d = D // H
+    F = llama_ffn_hidden_dim(args)
+    return {"attention_norm": (D,), "ffn_norm": (D,), "wq": (H * d, D), "wk": (Hkv * d, D), "wv": (Hkv * d, D),
+            "wo": (D, H * d), "w1": (F, D), "w3": (F, D), "w2": (D, F)}
+
+
+def check_block_tensors(args: ModelArgs, weights, cache_k, cache_v, x, out, bsz: int, seqlen: int) -> None:
+    """The C ABI receives bare pointers and derives every extent from ``args``.  When
+    the caller passes tensors, their shapes are checked here, on the host, before a
+    kernel could read or write past them: each weight against the shape ``args``
+    implies (the FFN width from dim, multiple_of and ffn_dim_multiplier), the caches
+    against [max_batch_size, max_seq_len, n_kv_heads, head_dim], x and out against
+    bsz * seqlen rows of dim.  Raw pointers (ints) are passed through unchecked."""
+    def numel(t):
+        return None if t is None or isinstance(t, int) else t.numel()
+    if isinstance(weights, dict):
+        for name, shape in block_tensor_shapes(args).items():
+            t = weights[name]
+            if not isinstance(t, int) and tuple(t.shape) != shape:
+                raise ValueError(f"weight {name} has shape {tuple(t.shape)}; the model arguments imply {shape}")
+    Hkv = args.n_kv_heads or args.n_heads
+    cache = args.max_batch_size * args.max_seq_len * Hkv * (args.dim // args.n_heads)
+    for name, t in (("cache_k", cache_k), ("cache_v", cache_v)):
+        n = numel(t)
+        if n is not None and n < cache:
+            raise ValueError(f"{name} holds {n} elements; max_batch_size x max_seq_len x n_kv_heads x head_dim "
+                             f"is {cache}")
+    act = bsz * seqlen * args.dim
+    for name, t in (("x", x), ("out", out)):
+        n = numel(t)
+        if n is not None and n < act:
+            raise ValueError(f"{name} holds {n} elements; bsz x seqlen x dim is {act}")
+
+
 def block_weights(tensors: dict) -> CBlockWeights:
-    return CBlockWeights(*[_ptr(tensors[n]) for n in
-                           ("attention_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w1", "w2", "w3")])
+    return CBlockWeights(*[_ptr(tensors[n]) for n in BLOCK_TENSORS])
 
 
 def llama_block_forward(args: ModelArgs, weights, cache_k, cache_v, freqs, freqs_end: int, x, out, bsz: int,
                         seqlen: int, start_pos: int, ws, ws_bytes: int, stream=None) -> None:
+    check_block_tensors(args, weights, cache_k, cache_v, x, out, bsz, seqlen)
     w = weights if isinstance(weights, CBlockWeights) else block_weights(weights)
     _check(lib().llama_block_forward(ctypes.byref(args.c()), ctypes.byref(w), _ptr(cache_k), _ptr(cache_v),
                                      _ptr(freqs), freqs_end, _ptr(x), _ptr(out), bsz, seqlen, start_pos, _ptr(ws),
@@ -241,6 +282,7 @@ def llama_block_forward(args: ModelArgs, weights, cache_k, cache_v, freqs, freqs
 def llama_block_decode_at(args: ModelArgs, weights, cache_k, cache_v, freqs, freqs_end: int, x, out, bsz: int,
                           start_pos_dev, max_start_pos: int, ws, ws_bytes: int, stream=None) -> None:
     """One-token block decode at the position held in ``start_pos_dev`` (device int32)."""
+    check_block_tensors(args, weights, cache_k, cache_v, x, out, bsz, 1)
     w = weights if isinstance(weights, CBlockWeights) else block_weights(weights)
     _check(lib().llama_block_decode_at(ctypes.byref(args.c()), ctypes.byref(w), _ptr(cache_k), _ptr(cache_v),
                                        _ptr(freqs), freqs_end, _ptr(x), _ptr(out), bsz, _ptr(start_pos_dev),
@@ -251,6 +293,7 @@ def llama_block_decode_at(args: ModelArgs, weights, cache_k, cache_v, freqs, fre
 def llama_block_forward_events(args: ModelArgs, weights, cache_k, cache_v, freqs, freqs_end: int, x, out, bsz: int,
                                seqlen: int, start_pos: int, ws, ws_bytes: int, events, stream=None) -> None:
     """``events``: 8 torch.cuda.Event(enable_timing=True) (or raw hipEvent_t handles)."""
+    check_block_tensors(args, weights, cache_k, cache_v, x, out, bsz, seqlen)
     w = weights if isinstance(weights, CBlockWeights) else block_weights(weights)
     st = _stream(stream)
     handles = []

@@ -25,6 +25,17 @@ inline size_t elem_size(llama_dtype dt) { return dt == LLAMA_BF16 ? 2 : 4; }
 inline bool dtype_ok(int dt) { return dt == LLAMA_F32 || dt == LLAMA_BF16; }
 inline int hip_status(hipError_t e) { return e == hipSuccess ? LLAMA_OK : LLAMA_ERR_HIP; }
 
+// Alignment the kernels rely on: tensors are read and written with 16-byte
+// vectors and global -> LDS DMA of 16-byte chunks; int32 id/position arrays and
+// per-row floats are read element-wise.  A null pointer counts as aligned (the
+// null checks are separate).
+inline bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+inline bool al4(const void* p) { return ((uintptr_t)p & 3) == 0; }
+template <typename... P>
+inline bool all_al16(const P*... p) {
+  return (al16(p) && ...);
+}
+
 struct Dims {
   int D, H, Hkv, d, F, n_rep;
 };
@@ -285,6 +296,7 @@ int llama_rmsnorm(const void* x, const void* w, void* y, int64_t rows, int32_t d
   if (!dtype_ok(dt) || rows < 0 || dim < 1 || !(eps >= 0.f)) return LLAMA_ERR_INVALID_ARG;
   if (rows == 0) return LLAMA_OK;
   if (!x || !w || !y) return LLAMA_ERR_INVALID_ARG;
+  if (!all_al16(x, w, y)) return LLAMA_ERR_INVALID_ARG;
   if (dim % (dt == LLAMA_BF16 ? 8 : 4)) return LLAMA_ERR_INVALID_ARG;
   if (rows > INT32_MAX) return LLAMA_ERR_INVALID_ARG;
   hipStream_t st = (hipStream_t)stream;
@@ -301,6 +313,7 @@ int llama_rope(void* xq, void* xk, const float* freqs, int32_t freqs_end, int32_
     return LLAMA_ERR_INVALID_ARG;
   if (xk && n_kv_heads < 1) return LLAMA_ERR_INVALID_ARG;
   if ((int64_t)start_pos + seqlen > freqs_end) return LLAMA_ERR_INVALID_ARG;
+  if (!all_al16(xq, xk, freqs)) return LLAMA_ERR_INVALID_ARG;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (dt == LLAMA_BF16) {
@@ -324,6 +337,7 @@ int llama_gqa_attn_prefill(const void* xq, const void* xk, const void* xv, void*
   rc = call_shape(a, bsz, seqlen, start_pos);
   if (rc != LLAMA_OK) return rc;
   if (!xq || !xk || !xv || !cache_k || !cache_v || !out) return LLAMA_ERR_INVALID_ARG;
+  if (!all_al16(xq, xk, xv, cache_k, cache_v, out)) return LLAMA_ERR_INVALID_ARG;
   hipStream_t st = (hipStream_t)stream;
   llama::AttnShape sh{bsz, seqlen, start_pos, g.H, g.Hkv, g.d, a->max_seq_len};
   hipError_t e;
@@ -350,8 +364,9 @@ int llama_gqa_attn_decode(const void* xq, const void* xk, const void* xv, void* 
   if (rc != LLAMA_OK) return rc;
   if (!xq || !xk || !xv || !cache_k || !cache_v || !out) return LLAMA_ERR_INVALID_ARG;
   const size_t need = decode_partial_floats(g, bsz, start_pos + 1, dt) * sizeof(float);
-  if (ws_bytes < need) return LLAMA_ERR_WORKSPACE_TOO_SMALL;
   if (need && !ws) return LLAMA_ERR_INVALID_ARG;
+  if (!all_al16(xq, xk, xv, cache_k, cache_v, out, need ? ws : nullptr)) return LLAMA_ERR_INVALID_ARG;
+  if (ws_bytes < need) return LLAMA_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = (hipStream_t)stream;
   llama::AttnShape sh{bsz, 1, start_pos, g.H, g.Hkv, g.d, a->max_seq_len};
   hipError_t e;
@@ -375,6 +390,7 @@ int llama_linear(const void* x, const void* w, void* y, int64_t rows, int32_t in
   if (rows == 0) return LLAMA_OK;
   if (!x || !w || !y || rows > INT32_MAX) return LLAMA_ERR_INVALID_ARG;
   if (in % (dt == LLAMA_BF16 ? 8 : 4) || outf % 4) return LLAMA_ERR_INVALID_ARG;
+  if (!all_al16(x, w, y)) return LLAMA_ERR_INVALID_ARG;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (dt == LLAMA_BF16) {
@@ -398,6 +414,7 @@ int llama_swiglu_ffn(const void* x, const void* w1, const void* w3, const void* 
   llama_ffn_workspace_size(rows, dim, hidden, dt, &need);
   if (rows == 0) return LLAMA_OK;
   if (!x || !w1 || !w3 || !w2 || !y || !ws) return LLAMA_ERR_INVALID_ARG;
+  if (!all_al16(x, w1, w3, w2, y, ws)) return LLAMA_ERR_INVALID_ARG;
   if (ws_bytes < need) return LLAMA_ERR_WORKSPACE_TOO_SMALL;
   const int M = (int)rows;
   const bool bf = dt == LLAMA_BF16;
@@ -441,7 +458,8 @@ static int block_forward_impl(const llama_model_args* a, const llama_block_weigh
   if (!w->attention_norm || !w->wq || !w->wk || !w->wv || !w->wo || !w->ffn_norm || !w->w1 || !w->w2 || !w->w3)
     return LLAMA_ERR_INVALID_ARG;
   if ((int64_t)start_pos + seqlen > freqs_end) return LLAMA_ERR_INVALID_ARG;
-  if (((uintptr_t)freqs) % 16 || ((uintptr_t)x) % 16 || ((uintptr_t)out) % 16 || ((uintptr_t)ws) % 16)
+  if (!all_al16(freqs, x, out, ws, cache_k, cache_v, w->attention_norm, w->wq, w->wk, w->wv, w->wo, w->ffn_norm,
+                w->w1, w->w2, w->w3))
     return LLAMA_ERR_INVALID_ARG;
   const size_t act = (size_t)bsz * seqlen * g.D * elem_size(dt);
   if (overlaps(x, act, out, act)) return LLAMA_ERR_INVALID_ARG;
@@ -490,6 +508,7 @@ int llama_embedding(const int32_t* tokens, const void* table, void* out, int64_t
   if (n == 0) return LLAMA_OK;
   if (!tokens || !table || !out) return LLAMA_ERR_INVALID_ARG;
   if (dim % (dt == LLAMA_BF16 ? 8 : 4)) return LLAMA_ERR_INVALID_ARG;
+  if (!al4(tokens) || !all_al16(table, out)) return LLAMA_ERR_INVALID_ARG;
   hipStream_t st = (hipStream_t)stream;
   if (dt == LLAMA_BF16)
     return hip_status(llama::embedding<bf16>(tokens, (const bf16*)table, (bf16*)out, n, dim, vocab, st));
@@ -504,6 +523,7 @@ int llama_lm_head_argmax(const void* h, int64_t h_row_stride, const void* norm_w
   if (!h || !norm_w || !w_out || !logits || !next || !ws) return LLAMA_ERR_INVALID_ARG;
   if (dim % (dt == LLAMA_BF16 ? 8 : 4) || vocab % 4 || h_row_stride % (dt == LLAMA_BF16 ? 8 : 4))
     return LLAMA_ERR_INVALID_ARG;
+  if (!all_al16(h, norm_w, w_out, logits, ws) || !al4(next)) return LLAMA_ERR_INVALID_ARG;
   size_t need = 0;
   llama_lm_head_workspace_size(bsz, dim, vocab, dt, &need);
   if (ws_bytes < need) return LLAMA_ERR_WORKSPACE_TOO_SMALL;
@@ -536,6 +556,7 @@ int llama_sample_top_p(const float* logits, int32_t* next, int32_t bsz, int32_t 
                        float top_p, const float* uniforms, llama_stream_t stream) {
   if (!logits || !next || bsz < 1 || vocab < 1) return LLAMA_ERR_INVALID_ARG;
   if (temperature != temperature || top_p != top_p) return LLAMA_ERR_INVALID_ARG;
+  if (!al16(logits) || !al4(next) || !al4(uniforms)) return LLAMA_ERR_INVALID_ARG;
   hipStream_t st = (hipStream_t)stream;
   if (!(temperature > 0.f)) return hip_status(llama::argmax_rows(logits, next, bsz, vocab, st));
   if (!uniforms) return LLAMA_ERR_INVALID_ARG;

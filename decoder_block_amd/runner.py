@@ -18,13 +18,7 @@ def check_weight_shapes(args: L.ModelArgs, weights: Dict[str, torch.Tensor]) -> 
     """The C ABI receives bare pointers and derives every extent from ``args`` (the
     FFN width from dim, multiple_of and ffn_dim_multiplier): weights of another shape
     would be read out of bounds, so their shapes are checked here, on the host."""
-    D, H = args.dim, args.n_heads
-    Hkv = args.n_kv_heads or H
-    d = D // H
-    F = L.llama_ffn_hidden_dim(args)
-    want = {"attention_norm": (D,), "ffn_norm": (D,), "wq": (H * d, D), "wk": (Hkv * d, D), "wv": (Hkv * d, D),
-            "wo": (D, H * d), "w1": (F, D), "w3": (F, D), "w2": (D, F)}
-    for name, shape in want.items():
+    for name, shape in L.block_tensor_shapes(args).items():
         got = tuple(weights[name].shape)
         if got != shape:
             raise ValueError(f"weight {name} has shape {got}; the model arguments imply {shape}")

@@ -23,7 +23,11 @@
  *    round-to-nearest-even rounding per stored value) or LLAMA_F32.  Every
  *    tensor of a call has the call's dtype unless stated otherwise (the RoPE
  *    table and LM-head logits are always fp32, token ids int32).
- *  - Device pointers must be 16-byte aligned.
+ *  - Device pointers must be 16-byte aligned (tensors are moved in 16-byte
+ *    vectors and global -> LDS copies), except int32 arrays (token ids, chosen
+ *    ids, the device-resident position) and the per-row uniforms of
+ *    llama_sample_top_p, which need 4-byte alignment.  A misaligned pointer is
+ *    rejected with LLAMA_ERR_INVALID_ARG.
  *  - Device entry points only enqueue work on `stream` (a hipStream_t; NULL is
  *    the default stream) and return without synchronising.  Results are ready
  *    when the stream reaches that point.
@@ -136,8 +140,8 @@ int llama_rmsnorm(const void* x, const void* w, void* y, int64_t rows, int32_t d
  * [bsz][seqlen][n_heads][head_dim] and xk [bsz][seqlen][n_kv_heads][head_dim] at
  * sequence index s has each interleaved pair (u[2i], u[2i+1]) rotated by the angle of
  * freqs_cis[start_pos + s][i] (a llama_rope_freqs table with freqs_end rows).
- * xk may be NULL (only q rotated).  Requires head_dim even,
- * start_pos + seqlen <= freqs_end. */
+ * xk may be NULL (only q rotated).  Requires head_dim a multiple of 4 (two
+ * pairs per vector), start_pos + seqlen <= freqs_end. */
 int llama_rope(void* xq, void* xk, const float* freqs_cis, int32_t freqs_end, int32_t bsz,
                int32_t seqlen, int32_t start_pos, int32_t n_heads, int32_t n_kv_heads,
                int32_t head_dim, llama_dtype dtype, llama_stream_t stream);

@@ -194,3 +194,83 @@ def test_runner_rejects_weights_of_another_shape():
         check_weight_shapes(model_args_for(w), wl.block_weights(w))
     ok = w.scaled(ffn_hidden=1536, ffn_dim_multiplier=0.25)
     check_weight_shapes(model_args_for(ok), wl.block_weights(ok))
+
+
+def test_every_device_pointer_must_be_aligned():
+    """Every tensor pointer an entry point passes to a kernel must be 16-byte aligned
+    (int32 id/position arrays and per-row uniforms 4-byte): one pointer at a time is
+    moved to an 8-byte (or 2-byte) boundary and the call must return INVALID_ARG.
+    Calls with a workspace pass one that is too small, so that a missing alignment
+    check would surface as WORKSPACE_TOO_SMALL; no call here reaches a launch."""
+    lib = dba.lib()
+    E, W = dba._lib.LLAMA_ERR_INVALID_ARG, dba._lib.LLAMA_ERR_WORKSPACE_TOO_SMALL
+    BF = dba.LLAMA_BF16
+    p = 1 << 20
+    m, m4 = p + 8, p + 2
+
+    def each(n, call, bad=m):
+        for i in range(n):
+            ptrs = [p] * n
+            ptrs[i] = bad
+            assert call(ptrs) == E, (call, i)
+
+    each(3, lambda q: lib.llama_rmsnorm(*q, 4, 256, 1e-5, BF, None))
+    each(3, lambda q: lib.llama_rope(*q, 64, 1, 9, 0, 4, 4, 64, BF, None))
+    each(3, lambda q: lib.llama_linear(*q, 4, 128, 64, BF, None))
+    a = dba.ModelArgs(dim=512, n_heads=4, n_kv_heads=2, max_batch_size=2, max_seq_len=8)
+    c = ctypes.byref(a.c())
+    each(6, lambda q: lib.llama_gqa_attn_prefill(*q, c, 1, 4, 0, BF, None))
+    big = dba.ModelArgs(dim=8192, n_heads=64, n_kv_heads=8, max_batch_size=1, max_seq_len=9000)
+    cb = ctypes.byref(big.c())
+    assert lib.llama_gqa_attn_decode(p, p, p, p, p, p, cb, 1, 8000, p, 16, BF, None) == W
+    each(7, lambda q: lib.llama_gqa_attn_decode(*q[:6], cb, 1, 8000, q[6], 16, BF, None))
+    assert lib.llama_swiglu_ffn(p, p, p, p, p, 4, 256, 768, p, 0, BF, None) == W
+    each(6, lambda q: lib.llama_swiglu_ffn(*q[:5], 4, 256, 768, q[5], 0, BF, None))
+    # the block: activations, caches, table, workspace and each of the nine weights
+    ba = dba.ModelArgs(dim=256, n_heads=2, n_kv_heads=1, max_batch_size=2, max_seq_len=16)
+    assert _raw_block_forward(ba) == W
+    for name in ("x", "ck", "cv", "freqs", "ws"):
+        assert _raw_block_forward(ba, **{name: m}) == E, name
+    assert _raw_block_forward(ba, out=2 * p + 8) == E
+    for i in range(9):
+        ptrs = [p] * 9
+        ptrs[i] = m
+        assert _raw_block_forward(ba, weights=L.CBlockWeights(*ptrs)) == E, i
+    assert _raw_decode_at(ba, ck=m) == E
+    # embedding: ids 4-byte, table and output 16-byte
+    assert lib.llama_embedding(m4, p, p, 4, 256, 10, BF, None) == E
+    each(2, lambda q: lib.llama_embedding(p, *q, 4, 256, 10, BF, None))
+    # output projection: h, norm weight, W_out, logits, workspace 16-byte; ids 4-byte
+    assert lib.llama_lm_head_argmax(p, 256, p, p, p, p, 2, 256, 1000, 1e-5, p, 0, BF, None) == W
+    each(4, lambda q: lib.llama_lm_head_argmax(q[0], 256, q[1], q[2], q[3], p, 2, 256, 1000, 1e-5, p, 0, BF, None))
+    assert lib.llama_lm_head_argmax(p, 256, p, p, p, p, 2, 256, 1000, 1e-5, m, 0, BF, None) == E
+    assert lib.llama_lm_head_argmax(p, 256, p, p, p, m4, 2, 256, 1000, 1e-5, p, 0, BF, None) == E
+    # sampling: logits 16-byte, ids and uniforms 4-byte
+    assert lib.llama_sample_top_p(m, p, 4, 100, 0.8, 0.9, p, None) == E
+    assert lib.llama_sample_top_p(p, m4, 4, 100, 0.8, 0.9, p, None) == E
+    assert lib.llama_sample_top_p(p, p, 4, 100, 0.8, 0.9, m4, None) == E
+
+
+def test_binding_checks_tensor_extents_before_the_call():
+    """Callers that pass tensors straight to the binding (not through BlockRunner) get
+    the same host-side extent checks: weights against the shapes the model arguments
+    imply, the caches and the activations against the call's extents."""
+    import torch
+    from decoder_block_amd.runner import model_args_for
+    w = wl.Workload(41, "extents", "bf16", 256, 2, 1, 768, 256, None, 1e-5, 1e4, batch=2, prefill_len=4,
+                    decode_steps=0)
+    a = model_args_for(w)
+    wts = wl.block_weights(w)
+    shape = (w.batch, w.max_seq_len, w.n_kv_heads, w.head_dim)
+    ck, cv = torch.zeros(shape, dtype=torch.bfloat16), torch.zeros(shape, dtype=torch.bfloat16)
+    x = torch.zeros(w.batch, 4, w.dim, dtype=torch.bfloat16)
+    out = torch.empty_like(x)
+    bad = dict(wts, w2=wts["w2"][:, :512].contiguous())
+    with pytest.raises(ValueError, match="w2"):
+        dba.llama_block_forward(a, bad, ck, cv, 1 << 20, 16, x, out, 2, 4, 0, 1 << 20, 0)
+    with pytest.raises(ValueError, match="cache_k"):
+        dba.llama_block_forward(a, wts, ck[:1], cv, 1 << 20, 16, x, out, 2, 4, 0, 1 << 20, 0)
+    with pytest.raises(ValueError, match="out"):
+        dba.llama_block_forward(a, wts, ck, cv, 1 << 20, 16, x, out[:1], 2, 4, 0, 1 << 20, 0)
+    with pytest.raises(ValueError, match="x"):
+        dba.llama_block_decode_at(a, wts, ck, cv, 1 << 20, 16, x[:, :1][:1], out, 2, 1 << 20, 3, 1 << 20, 0)
