@@ -195,10 +195,22 @@ def _args(H, Hkv, d, maxB, maxS, dtype_dim_mult=1):
 ])
 def test_attn_prefill(dtype, B, S, p0, H, Hkv, d):
     need_gpu()
-    print(f"case attn_prefill {dtype} B={B} S={S} p0={p0} H={H} Hkv={Hkv} d={d}", flush=True)
+    _attn_prefill_case(dtype, B, S, p0, H, Hkv, d)
+
+
+def _spike(cache_rows, positions, factor):
+    """Scale whole key rows (all kv heads) at the given positions: scores against them
+    jump by that factor, so the running maximum moves in the middle of a row."""
+    for t in positions:
+        cache_rows[:, t] = (cache_rows[:, t].float() * factor).to(cache_rows.dtype)
+
+
+def _attn_prefill_case(dtype, B, S, p0, H, Hkv, d, qstd=1.0, spikes=(), factor=1.0):
+    print(f"case attn_prefill {dtype} B={B} S={S} p0={p0} H={H} Hkv={Hkv} d={d} q std {qstd} "
+          f"key spikes {list(spikes)} x{factor}", flush=True)
     maxS = p0 + S + 3
     args = _args(H, Hkv, d, B + 1, maxS)
-    q = rnd((B, S, H, d), 1.0, dtype)
+    q = rnd((B, S, H, d), qstd, dtype)
     k = rnd((B, S, Hkv, d), 1.0, dtype)
     v = rnd((B, S, Hkv, d), 1.0, dtype)
     ck = torch.zeros(B + 1, maxS, Hkv, d, dtype=tdt(dtype))
@@ -206,6 +218,8 @@ def test_attn_prefill(dtype, B, S, p0, H, Hkv, d):
     if p0:
         ck[:, :p0] = rnd((B + 1, p0, Hkv, d), 1.0, dtype)
         cv[:, :p0] = rnd((B + 1, p0, Hkv, d), 1.0, dtype)
+    _spike(ck, [t for t in spikes if t < p0], factor)
+    _spike(k, [t - p0 for t in spikes if p0 <= t < p0 + S], factor)
     gck, gcv = dev(ck), dev(cv)
     out = torch.empty(B, S, H * d, dtype=tdt(dtype), device="cuda:0")
     dba.llama_gqa_attn_prefill(dev(q), dev(k), dev(v), gck, gcv, out, args, B, S, p0)
@@ -217,6 +231,21 @@ def test_attn_prefill(dtype, B, S, p0, H, Hkv, d):
     np.testing.assert_array_equal(f64(gcv), rcv)
     ref = ob.gqa_attention(f64(q), rck, rcv, p0)
     check(out, ref, dtype, "attn prefill")
+
+
+@pytest.mark.parametrize("B,S,p0,H,Hkv,d,qstd,spikes,factor", [
+    (2, 300, 0, 8, 2, 128, 10.0, (), 1.0),                   # scores spread over tens of units
+    (2, 300, 0, 8, 2, 128, 1.0, (3, 140, 141, 290), 30.0),  # single keys far above the rest, mid-row
+    (1, 200, 100, 4, 1, 64, 8.0, (20, 150, 299), 20.0),     # cached and new spikes, MQA, head_dim 64
+    (2, 130, 0, 8, 8, 128, 16.0, (64, 65), 8.0),            # MHA, spikes at a tile boundary
+])
+def test_attn_prefill_sharp_softmax(B, S, p0, H, Hkv, d, qstd, spikes, factor):
+    """Sharp score distributions (the pages take the softmax in fp32 after the -inf
+    mask): the kernel keeps its running maximum until some row's maximum grows by
+    more than 8 in log2 units, so these cases move it in the middle of rows, from
+    key tiles of one block to the next, against the oracle's exact softmax."""
+    need_gpu()
+    _attn_prefill_case("bf16", B, S, p0, H, Hkv, d, qstd, spikes, factor)
 
 
 def test_attn_prefill_sequences_in_cache_sized_groups():
@@ -280,11 +309,12 @@ def test_attn_decode_seeded_shapes():
         _attn_decode_case("bf16", B, p0, Hkv * n_rep, Hkv, d)
 
 
-def _attn_decode_case(dtype, B, p0, H, Hkv, d):
-    print(f"case attn_decode {dtype} B={B} p0={p0} H={H} Hkv={Hkv} d={d}", flush=True)
+def _attn_decode_case(dtype, B, p0, H, Hkv, d, qstd=1.0, spikes=(), factor=1.0):
+    print(f"case attn_decode {dtype} B={B} p0={p0} H={H} Hkv={Hkv} d={d} q std {qstd} "
+          f"key spikes {list(spikes)} x{factor}", flush=True)
     maxS = p0 + 2
     args = _args(H, Hkv, d, B, maxS)
-    q = rnd((B, 1, H, d), 1.0, dtype)
+    q = rnd((B, 1, H, d), qstd, dtype)
     k = rnd((B, 1, Hkv, d), 1.0, dtype)
     v = rnd((B, 1, Hkv, d), 1.0, dtype)
     ck = torch.zeros(B, maxS, Hkv, d, dtype=tdt(dtype))
@@ -292,6 +322,9 @@ def _attn_decode_case(dtype, B, p0, H, Hkv, d):
     if p0:
         ck[:, :p0] = rnd((B, p0, Hkv, d), 1.0, dtype)
         cv[:, :p0] = rnd((B, p0, Hkv, d), 1.0, dtype)
+    _spike(ck, [t for t in spikes if t < p0], factor)
+    if p0 in spikes:
+        k = (k.float() * factor).to(k.dtype)
     gck, gcv = dev(ck), dev(cv)
     out = torch.empty(B, 1, H * d, dtype=tdt(dtype), device="cuda:0")
     nbytes = dba.llama_attn_decode_workspace_size(args, B, p0)
@@ -305,6 +338,23 @@ def _attn_decode_case(dtype, B, p0, H, Hkv, d):
     np.testing.assert_array_equal(f64(gck), rck)
     ref = ob.gqa_attention(f64(q), rck, rcv, p0)
     check(out, ref, dtype, "attn decode")
+
+
+@pytest.mark.parametrize("B,p0,H,Hkv,d,qstd,spikes,factor", [
+    (1, 8300, 32, 8, 128, 1.0, (5, 2000, 4100, 8250, 8300), 30.0),   # dozens of splits, four-wave merge
+    (1, 8300, 32, 8, 128, 12.0, (), 1.0),                            # every split sharp
+    (4, 1500, 8, 2, 128, 1.0, (7, 700, 1499), 25.0),                 # about a dozen splits, one-wave merge
+    (2, 300, 8, 2, 64, 10.0, (150, 300), 20.0),                      # three splits, head_dim 64
+    (16, 1500, 16, 8, 128, 1.0, (100, 900, 1400), 30.0),             # one 8-wave workgroup per unit, no split
+])
+def test_attn_decode_sharp_softmax(B, p0, H, Hkv, d, qstd, spikes, factor):
+    """Sharp score distributions in decode: single keys far above the rest (in
+    different splits, so the split maxima differ by tens of units and the
+    log-sum-exp merge weighs most splits by tiny factors) and queries of large
+    norm, against the oracle's exact softmax, for the split layouts of the
+    decode kernel and both merge kernels."""
+    need_gpu()
+    _attn_decode_case("bf16", B, p0, H, Hkv, d, qstd, spikes, factor)
 
 
 # ----------------------------------------------------------------------------- config-5 pieces
@@ -325,7 +375,7 @@ def test_embedding_and_lm_head_argmax(B):
     # tile of the small-M projection, whose k-tiles are summed in a tile-dependent
     # (rotated) order: equal rows in different tiles agree only to rounding.
     w_out[77] = w_out[100]
-    norm_w = torch.ones(D, dtype=torch.bfloat16)
+    norm_w = (1.0 + rnd((D,), 0.2)).to(torch.bfloat16)      # a non-unit final-norm weight
     logits = torch.empty(B, V, dtype=torch.float32, device="cuda:0")
     nxt = torch.empty(B, dtype=torch.int32, device="cuda:0")
     nbytes = dba.llama_lm_head_workspace_size(B, D, V, dba.LLAMA_BF16)

@@ -19,6 +19,13 @@ from tests.gpu_util import check, f64, need_gpu
 pytestmark = pytest.mark.gpu
 
 
+# RMSNorm weights 1 + N(0, 0.2^2), distinct per norm and layer: the five workloads
+# use unit weights, so these tests exercise the gain multiply of each fused
+# normalisation (row-scale form, one-to-four-token weight streams, the split
+# reduction of 5-64 tokens) and the bf16 rounding of x * g
+GAINS = "normal"
+
+
 def _w64(wts):
     return {k: v.to(torch.float64).numpy() for k, v in wts.items()}
 
@@ -127,7 +134,8 @@ def test_llama2_70b_block_decode_batch32():
 
 def test_block_decode_seeded_shapes():
     """Ten one-token block calls with shapes from a seeded generator (head_dim
-    64/128, 1-8 kv heads, n_rep 1-8, batch 1-80 over 1-1500 cached N(0,1) rows):
+    64/128, 1-8 kv heads, n_rep 1-8, batch 1-80 over 1-1500 cached N(0,1) rows,
+    non-unit RMSNorm weights):
     weight streams with the norms fused (1-4 tokens), small-M tiles with wo's
     split reduction fused with ffn_norm (5-64), large tiles beyond; outputs and
     the appended cache rows against the oracle."""
@@ -146,7 +154,7 @@ def test_block_decode_seeded_shapes():
         B = int(g.integers(1, 5) if i % 3 == 0 else (g.integers(5, 65) if i % 3 == 1 else g.integers(65, 81)))
         p0 = int(g.integers(1, 1501))
         w = wl.Workload(200 + i, f"seeded-{i}", "bf16", D, H, Hkv, F, mo, None, 1e-5, 1e4, batch=B, prefill_len=0,
-                        decode_steps=1, cache_prefill=p0)
+                        decode_steps=1, cache_prefill=p0, norm_gains=GAINS)
         print(f"case {w.name}: D={D} H={H} Hkv={Hkv} d={d} F={F} B={B} decode at {p0}", flush=True)
         wts = wl.block_weights(w)
         x = wl.activations(w)
@@ -166,7 +174,7 @@ def test_block_decode_seeded_shapes():
 def test_block_prefill_seeded_shapes():
     """Eight block prefill calls with shapes from a seeded generator (head_dim
     64/128, 1-8 kv heads, n_rep 1-8, batch 1-4, 5-700 new tokens after 0-500
-    cached N(0,1) rows): ragged token counts on every GEMM tile family, the
+    cached N(0,1) rows, non-unit RMSNorm weights): ragged token counts on every GEMM tile family, the
     attention's head grouping and causal offsets; outputs and the appended cache
     rows against the oracle."""
     dev = need_gpu()
@@ -185,7 +193,7 @@ def test_block_prefill_seeded_shapes():
         S = int(g.integers(5, 701))
         p0 = int(g.choice([0, int(g.integers(1, 501))]))
         w = wl.Workload(300 + i, f"seeded-prefill-{i}", "bf16", D, H, Hkv, F, mo, None, 1e-5, 1e4, batch=B,
-                        prefill_len=S, decode_steps=0, cache_prefill=p0)
+                        prefill_len=S, decode_steps=0, cache_prefill=p0, norm_gains=GAINS)
         print(f"case {w.name}: D={D} H={H} Hkv={Hkv} d={d} F={F} B={B} S={S} at {p0}", flush=True)
         wts = wl.block_weights(w)
         x = wl.activations(w)[:, :S].contiguous()
@@ -204,30 +212,30 @@ def test_block_prefill_seeded_shapes():
 
 # ----------------------------------------------------------------------------- invariants
 SMALL = wl.Workload(30, "small-gqa", "bf16", 512, 8, 2, 1536, 256, None, 1e-5, 1e4, batch=3, prefill_len=100,
-                    decode_steps=6)
+                    decode_steps=6, norm_gains=GAINS)
 # 8 kv heads of head_dim 128: decode attention takes its one-workgroup-per-row layout
 SMALL_ROWS = wl.Workload(31, "small-gqa-8kv", "bf16", 2048, 16, 8, 1536, 256, 0.25, 1e-5, 5e5, batch=3,
-                         prefill_len=100, decode_steps=6)
+                         prefill_len=100, decode_steps=6, norm_gains=GAINS)
 
 
 # one to four tokens per decode step run the weight-streaming projections with the
 # normalisation fused; dim 640 = 512 + 128 and hidden 1712 = 3 * 512 + 176 end in
 # ragged chunks, and a single kv head serves all five query heads
 RAGGED4 = wl.Workload(32, "ragged-640-b4", "bf16", 640, 5, 1, 1712, 8, None, 1e-5, 1e4, batch=4, prefill_len=45,
-                      decode_steps=4)
+                      decode_steps=4, norm_gains=GAINS)
 # six tokens per decode step: the split-K projections of the tiled kernels, with
 # wo's split reduction fused with the residual add and ffn_norm
 SMALL_ROWS6 = wl.Workload(34, "small-gqa-8kv-b6", "bf16", 2048, 16, 8, 1536, 256, 0.25, 1e-5, 5e5, batch=6,
-                          prefill_len=100, decode_steps=4)
+                          prefill_len=100, decode_steps=4, norm_gains=GAINS)
 # 16 sequences x 8 kv heads = 128 units: decode attention runs one 8-wave workgroup per
 # unit (no split), also with the position read from device memory
 SMALL_ROWS16 = wl.Workload(35, "small-gqa-8kv-b16", "bf16", 2048, 16, 8, 1536, 256, 0.25, 1e-5, 5e5, batch=16,
-                           prefill_len=100, decode_steps=4)
+                           prefill_len=100, decode_steps=4, norm_gains=GAINS)
 RAGGED1 = wl.Workload(33, "ragged-640-b1", "bf16", 640, 5, 1, 1712, 8, None, 1e-5, 1e4, batch=1, prefill_len=45,
-                      decode_steps=4)
+                      decode_steps=4, norm_gains=GAINS)
 # 40 tokens per decode step: 64-row tiles over 40 rows (a ragged row tail) with K split
 SMALL_ROWS40 = wl.Workload(36, "small-gqa-8kv-b40", "bf16", 2048, 16, 8, 1536, 256, 0.25, 1e-5, 5e5, batch=40,
-                           prefill_len=100, decode_steps=3)
+                           prefill_len=100, decode_steps=3, norm_gains=GAINS)
 
 
 def _small_runner(dev, batch=None, w=SMALL):

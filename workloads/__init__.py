@@ -15,11 +15,19 @@ Recipe (the same for every workload):
     pre-filled cache rows);
   * for bf16 workloads the float32 draw is rounded to bfloat16 with
     round-to-nearest-even (``tensor.to(torch.bfloat16)``);
-  * RMSNorm weights are ones; token ids are uniform in [0, vocab).
+  * RMSNorm weights are ones (the pages initialise them to ones, and the five
+    workloads state unit weights).  A test workload may instead draw them,
+    seeded per norm and per layer, so that a swapped or dropped gain changes
+    the result: ``norm_gains="normal"`` gives 1 + N(0, 0.2^2);
+    ``norm_gains="pow2"`` gives 2^k with k uniform in {-1, 0, 1}, for which
+    x * g is exact in bf16 (the 32-layer tests use it: there the bf16 rounding
+    of x * g, which the per-block tests cover with "normal" gains, would take
+    most of the error budget of a layer fed with the small embedding rows);
+  * token ids are uniform in [0, vocab).
 
 Tensor ids: 0 x_prefill, 1 x_decode, 2..8 wq wk wv wo w1 w2 w3,
 9/10 pre-filled cache k/v, 11 embedding, 12 output projection, 13 token ids,
-20 scratch for tests.
+14/15 attention_norm / ffn_norm gains, 16 final-norm gain, 20 scratch for tests.
 """
 from __future__ import annotations
 
@@ -35,6 +43,7 @@ T_X_PREFILL, T_X_DECODE = 0, 1
 T_WQ, T_WK, T_WV, T_WO, T_W1, T_W2, T_W3 = 2, 3, 4, 5, 6, 7, 8
 T_CACHE_K, T_CACHE_V = 9, 10
 T_EMBED, T_OUTPUT, T_TOKENS = 11, 12, 13
+T_ATTN_NORM, T_FFN_NORM, T_FINAL_NORM = 14, 15, 16
 T_TEST = 20
 
 WEIGHT_STD = 0.02
@@ -60,6 +69,7 @@ class Workload:
     cache_prefill: int = 0     # positions pre-filled with N(0,1) (decode-only workload)
     n_layers: int = 1
     vocab_size: int = 0
+    norm_gains: str = "ones"    # RMSNorm weights: "ones", "normal" or "pow2" (see the module docstring)
 
     @property
     def head_dim(self) -> int:
@@ -110,16 +120,30 @@ def tokens(shape: Tuple[int, ...], vocab: int, wid: int, layer: int = 0) -> torc
     return torch.randint(0, vocab, shape, generator=g, dtype=torch.int32)
 
 
+def norm_gain(w: Workload, layer: int, tid: int) -> torch.Tensor:
+    """An RMSNorm weight [dim] as the workload's ``norm_gains`` names it."""
+    if w.norm_gains == "ones":
+        return torch.ones(w.dim, dtype=torch_dtype(w.dtype))
+    g = torch.Generator().manual_seed(_seed(w.wid, layer, tid))
+    if w.norm_gains == "normal":
+        t = 1.0 + 0.2 * torch.randn(w.dim, generator=g, dtype=torch.float32)
+    elif w.norm_gains == "pow2":
+        t = torch.exp2(torch.randint(-1, 2, (w.dim,), generator=g).to(torch.float32))
+    else:
+        raise ValueError(f"unknown norm_gains {w.norm_gains!r}")
+    return t.to(torch_dtype(w.dtype))
+
+
 def block_weights(w: Workload, layer: int = 0) -> dict:
-    """Linear weights as nn.Linear stores them, [out, in]; norm weights are ones."""
+    """Linear weights as nn.Linear stores them, [out, in]; norm weights from norm_gain."""
     D, H, Hkv, d, F = w.dim, w.n_heads, w.n_kv_heads, w.head_dim, w.ffn_hidden
     shapes = {
         "wq": ((H * d, D), T_WQ), "wk": ((Hkv * d, D), T_WK), "wv": ((Hkv * d, D), T_WV),
         "wo": ((D, H * d), T_WO), "w1": ((F, D), T_W1), "w2": ((D, F), T_W2), "w3": ((F, D), T_W3),
     }
     out = {k: normal(s, WEIGHT_STD, w.dtype, w.wid, layer, tid) for k, (s, tid) in shapes.items()}
-    out["attention_norm"] = torch.ones(D, dtype=torch_dtype(w.dtype))
-    out["ffn_norm"] = torch.ones(D, dtype=torch_dtype(w.dtype))
+    out["attention_norm"] = norm_gain(w, layer, T_ATTN_NORM)
+    out["ffn_norm"] = norm_gain(w, layer, T_FFN_NORM)
     return out
 
 
@@ -150,10 +174,10 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
 
 
 def stack_tensors(w: Workload):
-    """Embedding [vocab, dim], final RMSNorm weight (ones) and output projection [vocab, dim]."""
+    """Embedding [vocab, dim], final RMSNorm weight (norm_gain) and output projection [vocab, dim]."""
     emb = normal((w.vocab_size, w.dim), WEIGHT_STD, w.dtype, w.wid, 0, T_EMBED)
     out = normal((w.vocab_size, w.dim), WEIGHT_STD, w.dtype, w.wid, 0, T_OUTPUT)
-    return emb, torch.ones(w.dim, dtype=torch_dtype(w.dtype)), out
+    return emb, norm_gain(w, 0, T_FINAL_NORM), out
 
 
 def prompt_tokens(w: Workload) -> torch.Tensor:
