@@ -1,16 +1,21 @@
 """Benchmark of the LLaMA decoder-block forward pass on one MI355X.
 
-One step = one ``llama_block_forward`` prefill call of the LLaMA-7B-shaped
-block (dim 4096, 32 heads, FFN 11008, bf16) over batch 4 x 2048 tokens: every
-step of the hot path (RMSNorm, QKV + RoPE + cache append, causal attention,
-wo + residual, RMSNorm, w1/w3 + SwiGLU, w2 + residual) on seeded synthetic
-inputs already resident in HBM.  ``value`` is prefill tokens/s for the block.
+One step = one prefill call of the 32-layer Llama-3-8B-shaped stack (dim 4096,
+32 query / 8 kv heads, FFN 14336, vocab 128256, bf16) over 64 prompts of 2048
+random token ids: the embedding gather, 32 x ``llama_block_forward`` (every
+step of the block: RMSNorm, QKV + RoPE + cache append, causal GQA attention,
+wo + residual, RMSNorm, w1/w3 + SwiGLU, w2 + residual), the final RMSNorm, the
+output projection of the last position and the greedy token, on seeded
+synthetic inputs already resident in HBM.  ``value`` is prefill tokens/s per
+block: 64 x 2048 tokens x 32 blocks / the step's wall time.
 
-Also reported on the same line: per-stage times from HIP events recorded on
-the launch stream, the MFMA roofline fraction of the dominant kernel, the
-Llama-3-8B-shaped prefill (1 x 8192) and decode steps (1 x T = 8193..) and the
-Llama-2-70B-shaped batch-32 decode step with its attention kernel's HBM
-roofline fraction, and the CPU oracle timed on a bounded sample.
+The same JSON line reports the stack's greedy decode (256 one-token steps from
+the prefilled caches, eager and replayed from one HIP graph, and with
+temperature + top-p sampling), per-stage times from HIP events recorded on the
+launch stream, the MFMA roofline fraction of the dominant kernel (the dual
+w1/w3 GEMM at M = 131072), the single-block workloads (LLaMA-7B-shaped prefill,
+Llama-3-8B-shaped prefill and decode, Llama-2-70B-shaped batch-32 decode, the
+tiny fp32 block) and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -177,20 +182,23 @@ def kernel_traffic(kernel_key):
         return None
 
 
-def cpu_baseline(w, wts, x):
-    """The oracle (numpy float64) on the same workload (a few seconds of BLAS work on the host)."""
-    import numpy as np
-    import torch
-    from oracle import block as ob
-    blas = "unknown"
+def blas_threads():
+    """(threads, library) of the BLAS numpy uses (the oracle's matrix products)."""
     try:
         from threadpoolctl import threadpool_info
         libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
         cores = max((i.get("num_threads", 1) for i in libs), default=1)
-        if libs:
-            blas = f"{libs[0].get('internal_api', '?')} {libs[0].get('version', '')}".strip()
+        blas = f"{libs[0].get('internal_api', '?')} {libs[0].get('version', '')}".strip() if libs else "unknown"
+        return int(cores), blas
     except Exception:
-        cores = os.cpu_count() or 1
+        return os.cpu_count() or 1, "unknown"
+
+
+def cpu_block_prefill(w, wts, x):
+    """The oracle (numpy float64) on a whole single-block prefill workload: tokens/s."""
+    import numpy as np
+    import torch
+    from oracle import block as ob
     S, B = w.prefill_len, w.batch
     W = {k: v.to(torch.float64).numpy() for k, v in wts.items()}
     xs = x[:, :S].to(torch.float64).numpy()
@@ -199,9 +207,8 @@ def cpu_baseline(w, wts, x):
     t0 = time.perf_counter()
     ob.block_forward(xs, W, ck, cv, 0, w.n_heads, w.n_kv_heads, w.norm_eps, w.rope_theta)
     dt = time.perf_counter() - t0
-    return {"value": B * S / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"the whole {w.name} workload ({B} x {S}-token prefill), numpy float64, {dt:.1f} s",
-            "blas": blas, "cpu": cpu_model()}
+    return {"tokens_per_s": round(B * S / dt, 1), "seconds": round(dt, 2),
+            "sample": f"the whole {w.name} workload ({B} x {S}-token prefill), numpy float64"}
 
 
 def cpu_model():
@@ -306,7 +313,9 @@ def bench_tiny(dev, cpu):
 def stack_oracle_sample(w):
     """The oracle on a bounded sample of the 32-layer workload: sequence 0 of 64,
     layers 0 and 1 (weights generated and upcast layer by layer), its 2048-token
-    prompt and then one one-token call; rates scaled to 32 layers."""
+    prompt and then one one-token call.  Returns the cpu_baseline object in the
+    headline's unit (prefill tokens/s per block) plus the decode step scaled to
+    32 layers."""
     import numpy as np
     import torch
     import workloads as wl
@@ -329,100 +338,145 @@ def stack_oracle_sample(w):
         t2 = time.perf_counter()
         t_pre += t1 - t0
         t_dec += t2 - t1
-    scale = w.n_layers / layers
-    return {"prefill_tokens_per_s": round(S / (t_pre * scale), 2), "decode_ms_per_step": round(t_dec * scale * 1e3, 1),
-            "kind": "oracle", "sample": f"sequence 0 of {w.batch}, layers 0-1 of {w.n_layers} (times scaled to "
-            f"{w.n_layers} layers; embedding and output projection not included), numpy float64"}
+    cores, blas = blas_threads()
+    return {"value": round(S * layers / t_pre, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"sequence 0 of {w.batch} ({S}-token prompt), layers 0-1 of {w.n_layers}, numpy float64: "
+                      f"{t_pre:.1f} s of prefill; prefill tokens/s per block = {S} tokens x {layers} blocks / that "
+                      f"time (embedding and output projection not included)",
+            "decode_ms_per_step_scaled_to_32_layers": round(t_dec * w.n_layers / layers * 1e3, 1),
+            "blas": blas, "cpu": cpu_model()}
 
 
-def bench_stack(dev, steps):
-    """32 layers + embedding + LM head: prefill of 64 x 2048 prompts, then greedy one-token steps."""
+def stack_layer_weights(w):
+    """The seeded weights of every layer, generated on host threads (torch's
+    generators release the GIL; each layer's draws are independent of the order)."""
+    import concurrent.futures as cf
+    import workloads as wl
+    with cf.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        return list(ex.map(lambda l: wl.block_weights(w, l), range(w.n_layers)))
+
+
+def bench_stack(dev, steps, warmup, decode_steps):
+    """The headline: 32 layers + embedding + LM head.  ``steps`` timed prefill calls of
+    64 x 2048 prompts (after ``warmup`` untimed ones), one more with stage events on
+    every layer, then ``decode_steps`` greedy one-token steps (eager, replayed from a
+    HIP graph, and sampled with temperature + top-p from a graph)."""
     import torch
     import workloads as wl
     from decoder_block_amd.model import StackRunner
     from decoder_block_amd.runner import model_args_for
     w = wl.WORKLOADS[5]
     log(f"workload {w.name}: generating {w.n_layers} layers")
+    layers = stack_layer_weights(w)
     emb, norm_w, w_out = wl.stack_tensors(w)
-    stack = StackRunner(model_args_for(w), lambda l: wl.block_weights(w, l), emb, norm_w, w_out, torch.bfloat16, dev)
+    stack = StackRunner(model_args_for(w), lambda l: layers[l], emb, norm_w, w_out, torch.bfloat16, dev)
+    del layers, emb, w_out
+    B, S = w.batch, w.prefill_len
+    decode_steps = min(decode_steps, w.decode_steps)
     prompt = wl.prompt_tokens(w).to(dev)
-    out = torch.empty(steps + 1, w.batch, dtype=torch.int32, device=dev)
-    logits = torch.empty(w.batch, w.vocab_size, dtype=torch.float32, device=dev)
-    stack.forward(prompt, 0, logits, out[0])          # warm-up (fills the caches)
+    out = torch.empty(decode_steps + 1, B, dtype=torch.int32, device=dev)
+    logits = torch.empty(B, w.vocab_size, dtype=torch.float32, device=dev)
+    log(f"stack prefill: {warmup} warm-up + {steps} timed steps")
+    for _ in range(warmup):
+        stack.forward(prompt, 0, logits, out[0])
     torch.cuda.synchronize()
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        stack.forward(prompt, 0, logits, out[0])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    log(f"stack prefill {wall * 1e3:.1f} ms")
+    # per-stage durations of every layer from HIP events recorded on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(w.n_layers)]
+    stack.forward(prompt, 0, logits, out[0], layer_events=evs)
+    torch.cuda.synchronize()
+    stage_ms = [sum(e[i - 1].elapsed_time(e[i]) for e in evs) / w.n_layers for i in range(1, 8)]
+    # greedy decode from the prefilled caches, eager
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     e[0].record()
-    stack.forward(prompt, 0, logits, out[0])
+    for t in range(decode_steps):
+        stack.forward(out[t].view(B, 1), S + t, logits, out[t + 1])
     e[1].record()
-    for t in range(steps):
-        stack.forward(out[t].view(w.batch, 1), w.prefill_len + t, logits, out[t + 1])
-    e[2].record()
     torch.cuda.synchronize()
-    pre = e[0].elapsed_time(e[1])
-    dec = e[1].elapsed_time(e[2]) / steps
-    log(f"stack prefill {pre:.1f} ms, decode {dec:.3f} ms/step")
+    dec = e[0].elapsed_time(e[1]) / decode_steps
+    log(f"stack decode {dec:.3f} ms/step")
     # the same steps replayed from one captured HIP graph (position held on the device)
     stack.forward(prompt, 0, logits, out[0])
     tok = out[0].clone()
-    pos = torch.full((1,), w.prefill_len, dtype=torch.int32, device=dev)
-    max_pos = w.prefill_len + steps
+    pos = torch.full((1,), S, dtype=torch.int32, device=dev)
+    max_pos = S + decode_steps - 1                       # the last position a timed step writes
     stack.decode_step_at(tok, pos, max_pos, logits)      # eager first step (loads the kernels)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         stack.decode_step_at(tok, pos, max_pos, logits)
+    pos.fill_(S)
+    tok.copy_(out[0])
     torch.cuda.synchronize()
     e[0].record()
-    for _ in range(steps):
+    for _ in range(decode_steps):
         graph.replay()
     e[1].record()
     torch.cuda.synchronize()
-    dec_g = e[0].elapsed_time(e[1]) / steps
+    dec_g = e[0].elapsed_time(e[1]) / decode_steps
     log(f"stack decode from a HIP graph {dec_g:.3f} ms/step")
     del graph
     # the same loop sampling with temperature 0.8 and top-p 0.95 (the walkthrough's
     # defaults); fresh uniforms are copied in between replays, as generate() does
-    pos.fill_(w.prefill_len)
+    pos.fill_(S)
     tok.copy_(out[0])
     gu = torch.Generator(device=dev).manual_seed(7)
-    us = torch.rand(steps + 1, w.batch, generator=gu, device=dev)
+    us = torch.rand(decode_steps + 1, B, generator=gu, device=dev)
     ubuf = us[0].clone()
     stack.decode_step_at(tok, pos, max_pos, logits, 0.8, 0.95, ubuf)      # eager first step
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         stack.decode_step_at(tok, pos, max_pos, logits, 0.8, 0.95, ubuf)
+    pos.fill_(S)
+    tok.copy_(out[0])
     torch.cuda.synchronize()
     e[0].record()
-    for t in range(steps):
+    for t in range(decode_steps):
         ubuf.copy_(us[t + 1])
         graph.replay()
     e[1].record()
     torch.cuda.synchronize()
-    dec_s = e[0].elapsed_time(e[1]) / steps
+    dec_s = e[0].elapsed_time(e[1]) / decode_steps
     log(f"stack sampled decode from a HIP graph {dec_s:.3f} ms/step")
     del graph
-    # top-p sampling of the last step's logits (temperature 0.8, top_p 0.95: the walkthrough's defaults)
+    # top-p sampling of the last step's logits alone
     g = torch.Generator(device=dev).manual_seed(5)
-    uni = torch.rand(20, w.batch, generator=g, device=dev)
+    uni = torch.rand(20, B, generator=g, device=dev)
     from decoder_block_amd import _lib as L
-    L.llama_sample_top_p(logits, out[0], w.batch, w.vocab_size, 0.8, 0.95, uni[0])
+    L.llama_sample_top_p(logits, out[0], B, w.vocab_size, 0.8, 0.95, uni[0])
     torch.cuda.synchronize()
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record()
+    e[0].record()
     for i in range(20):
-        L.llama_sample_top_p(logits, out[0], w.batch, w.vocab_size, 0.8, 0.95, uni[i])
-    s1.record()
+        L.llama_sample_top_p(logits, out[0], B, w.vocab_size, 0.8, 0.95, uni[i])
+    e[1].record()
     torch.cuda.synchronize()
-    samp = s0.elapsed_time(s1) / 20
-    res = {"prefill_ms": round(pre, 2), "prefill_tokens_per_s": round(w.batch * w.prefill_len / pre * 1e3, 1),
-           "decode_ms_per_step": round(dec, 3), "decode_tokens_per_s": round(w.batch / dec * 1e3, 1),
-           "graph_decode_ms_per_step": round(dec_g, 3), "graph_decode_tokens_per_s": round(w.batch / dec_g * 1e3, 1),
+    samp = e[0].elapsed_time(e[1]) / 20
+    work = stage_work(w, B, S, 0)
+    stages = {}
+    for name, ms in zip(STAGES, stage_ms):
+        kind, amount = work[name]
+        if kind == "mfma":
+            ach = amount / (ms * 1e-3) / 1e12
+            stages[name] = {"ms": round(ms, 4), "tflops": round(ach, 1), "mfma_frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+        else:
+            ach = amount / (ms * 1e-3) / 1e9
+            stages[name] = {"ms": round(ms, 4), "gbs": round(ach, 1), "hbm_frac": round(ach / PEAK_HBM_GBS, 4)}
+    res = {"wall_s": wall, "stage_ms": stage_ms, "work": work,
+           "prefill_ms": round(wall * 1e3, 2), "stack_prefill_tokens_per_s": round(B * S / wall, 1),
+           "layer_stages": stages,
+           "decode_ms_per_step": round(dec, 3), "decode_tokens_per_s": round(B / dec * 1e3, 1),
+           "graph_decode_ms_per_step": round(dec_g, 3), "graph_decode_tokens_per_s": round(B / dec_g * 1e3, 1),
            "graph_sampled_decode_ms_per_step": round(dec_s, 3),
-           "graph_sampled_decode_tokens_per_s": round(w.batch / dec_s * 1e3, 1),
-           "decode_steps_timed": steps, "batch": w.batch, "prompt": w.prefill_len, "layers": w.n_layers,
-           "top_p_sampling_us": round(samp * 1e3, 1)}
+           "graph_sampled_decode_tokens_per_s": round(B / dec_s * 1e3, 1),
+           "decode_steps_timed": decode_steps, "decode_positions": [S, S + decode_steps - 1], "batch": B,
+           "prompt": S, "layers": w.n_layers, "top_p_sampling_us": round(samp * 1e3, 1)}
     del stack
     torch.cuda.empty_cache()
-    return res
+    return w, res
 
 
 def bench_tp_share(dev, flush, reps):
@@ -481,45 +535,18 @@ def bench_tp_share(dev, flush, reps):
     return res
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    # (10 by default: after set-up, 3 untimed calls left the first timed window
-    # 2-8 % slow at identical kernel times)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--decode-steps", type=int, default=16, help="timed one-token calls per decode workload")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--prefill-only", action="store_true", help="skip the extra workloads (profiling runs)")
-    ap.add_argument("--stack", action="store_true",
-                    help="also time the 32-layer Llama-3-8B-shaped stack: 64 x 2048 prefill + greedy steps")
-    ap.add_argument("--calibration-copy", action="store_true",
-                    help="first run one plain 1 GiB device-to-device copy (scales rocprofv3 FETCH/WRITE_SIZE)")
-    a = ap.parse_args()
-    if a.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported (this build has no multi-GPU "
-              f"path)", file=sys.stderr)
-        sys.exit(2)
+SECTIONS = ("stack", "llama7b", "llama3_8b", "llama2_70b", "tiny")
 
+
+def bench_llama7b(dev, a, cpu):
+    """The LLaMA-7B-shaped block prefill (batch 4 x 2048, MHA): per-stage times and
+    the dual w1/w3 GEMM's fraction of the MFMA roofline at M = 8192."""
     import torch
     import workloads as wl
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda:0")
-    if a.calibration_copy:
-        src = torch.ones(1 << 29, dtype=torch.float16, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    # ---------------------------------------------------------------- headline: 7B-shaped block prefill
     log("workload llama7b-block-prefill: generating inputs")
     w2, wts2, r2 = make_runner(2, dev)
     x2 = wl.activations(w2).to(dev)
     tokens = w2.batch * w2.prefill_len
-    log(f"timing {a.steps} steps after {a.warmup} warmup")
     wall, stage_ms = time_prefill(r2, x2, a.steps, a.warmup)
     work = stage_work(w2, w2.batch, w2.prefill_len, 0)
     stages = {}
@@ -531,22 +558,88 @@ def main():
         else:
             ach = amount / (ms * 1e-3) / 1e9
             stages[name] = {"ms": round(ms, 4), "gbs": round(ach, 1), "hbm_frac": round(ach / PEAK_HBM_GBS, 4)}
-    dom = "w1w3_swiglu"
-    dom_ms = stage_ms[STAGES.index(dom)]
-    dom_ach = work[dom][1] / (dom_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": "gemm_bf16_dma<256x256x64, 8 waves, DUAL, EpiSwiGLU> (w1/w3 + SwiGLU)",
-                "achieved": round(dom_ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(dom_ach / PEAK_BF16_TFLOPS, 4), "traffic": kernel_traffic("w1w3_swiglu_llama7b"),
-                "kernel_ms": round(dom_ms, 4)}
-    total_gemm_attn = sum(work[n][1] for n in STAGES if work[n][0] == "mfma")
-    block_ach = total_gemm_attn / wall / 1e12
-    extra = {"block_tflops": round(block_ach, 1), "block_mfma_frac": round(block_ach / PEAK_BF16_TFLOPS, 4),
-             "stages": stages}
+    total = sum(work[n][1] for n in STAGES if work[n][0] == "mfma")
+    res = {"tokens_per_s": round(tokens / wall, 1), "ms": round(wall * 1e3, 4),
+           "block_tflops": round(total / wall / 1e12, 1), "block_mfma_frac": round(total / wall / 1e12 /
+                                                                                   PEAK_BF16_TFLOPS, 4),
+           "stages": stages, "w1w3_traffic_bytes": kernel_traffic("w1w3_swiglu_llama7b")}
     del r2
     torch.cuda.empty_cache()
+    if cpu:
+        res["cpu_oracle"] = cpu_block_prefill(w2, wts2, wl.activations(w2))
+    return res
 
-    if not a.prefill_only:
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20, help="timed steps (stack prefill calls; block prefill calls)")
+    # (10 by default: after set-up, 3 untimed calls left the first timed window
+    # 2-8 % slow at identical kernel times)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-steps", type=int, default=16,
+                    help="timed one-token calls of the single-block decode workloads")
+    ap.add_argument("--stack-decode-steps", type=int, default=256,
+                    help="greedy one-token steps of the 32-layer stack (the workload's 256)")
+    ap.add_argument("--sections", default=",".join(SECTIONS),
+                    help="comma-separated subset of " + ",".join(SECTIONS) + " (profiling runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="first run one plain 1 GiB device-to-device copy (scales rocprofv3 FETCH/WRITE_SIZE)")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported (this build has no multi-GPU "
+              f"path)", file=sys.stderr)
+        sys.exit(2)
+    sections = [x for x in a.sections.split(",") if x]
+    unknown = [x for x in sections if x not in SECTIONS]
+    if unknown:
+        print(f"unknown sections {unknown}; choose from {SECTIONS}", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as wl
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    cpu = not a.no_cpu_baseline
+    if a.calibration_copy:
+        src = torch.ones(1 << 29, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    extra = {}
+    value = wall = roofline = cpu_base = None
+    w5 = wl.WORKLOADS[5]
+    # ---------------------------------------------------------------- headline: the 32-layer stack
+    if "stack" in sections:
+        w5, st = bench_stack(dev, a.steps, a.warmup, a.stack_decode_steps)
+        wall = st.pop("wall_s")
+        stage_ms, work = st.pop("stage_ms"), st.pop("work")
+        value = w5.batch * w5.prefill_len * w5.n_layers / wall
+        dom = "w1w3_swiglu"
+        dom_ms = stage_ms[STAGES.index(dom)]
+        dom_ach = work[dom][1] / (dom_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": "gemm_bf16_dma<256x256x64, 8 waves, DUAL, EpiSwiGLU> (w1/w3 + SwiGLU, "
+                    "M = 131072, N = 2 x 14336, K = 4096)", "achieved": round(dom_ach, 1), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(dom_ach / PEAK_BF16_TFLOPS, 4),
+                    "traffic": kernel_traffic("w1w3_swiglu_llama3_8b_stack"), "kernel_ms": round(dom_ms, 4),
+                    "flops_per_launch": work[dom][1]}
+        extra["llama3_8b_stack"] = st
+        if cpu:
+            log("cpu oracle: bounded sample of the 32-layer stack")
+            cpu_base = stack_oracle_sample(w5)
+
+    if "llama7b" in sections:
+        extra["llama7b_block_prefill"] = bench_llama7b(dev, a, cpu)
+
+    flush = None
+    if "llama3_8b" in sections or "llama2_70b" in sections:
         flush = torch.zeros(1024 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    if "llama3_8b" in sections:
         # ------------------------------------------------------------ 8B-shaped prefill 8192 + decode
         log("workload llama3-8b-block: prefill 8192 then decode steps")
         w3, wts3, r3 = make_runner(3, dev)
@@ -578,9 +671,21 @@ def main():
                 "attention_us": round(st[2] * 1e3, 2), "attention_gbs": round(attn_gbs, 1),
                 "attention_hbm_frac": round(attn_gbs / PEAK_HBM_GBS, 4),
                 "step_gbs": round((wb + kvb) / (sum(tot) / len(tot) * 1e-3) / 1e9, 1),
+                "stage_us": {n: round(v * 1e3, 2) for n, v in zip(STAGES, st)},
                 "steps_timed": nd, "positions": [S3, S3 + nd - 1]}
         del r3
         torch.cuda.empty_cache()
+        if cpu:
+            import numpy as np
+            shape3 = (1, S3 + 1, w3.n_kv_heads, w3.head_dim)
+            x3d = wl.activations(w3)[:, S3:S3 + 1].contiguous()
+            dec3["cpu_oracle_step_us"] = round(cpu_decode_step_us(w3, wts3, x3d, np.zeros(shape3), np.zeros(shape3),
+                                                                  S3), 1)
+            dec3["cpu_oracle_note"] = ("oracle, numpy float64, one call at position 8192 over a zero cache of the "
+                                       "same shape (its cost depends on the shape only)")
+        extra["llama3_8b_prefill_8192"] = pre3
+        extra["llama3_8b_decode"] = dec3
+    if "llama2_70b" in sections:
         # ------------------------------------------------------------ 70B-shaped batch-32 decode
         log("workload llama2-70b-block-decode: batch 32 at position 4096")
         w4 = wl.WORKLOADS[4]
@@ -592,9 +697,9 @@ def main():
         st4 = [0.0] * 7
         for _ in range(max(a.decode_steps, 3)):
             # the same token at the same position each rep: the append rewrites identical rows
-            t, s = time_decode(r4, [x4], [p0], flush)
+            t, s_ = time_decode(r4, [x4], [p0], flush)
             tot4 += t
-            st4 = [u + v for u, v in zip(st4, s)]
+            st4 = [u + v for u, v in zip(st4, s_)]
         n4 = len(tot4)
         st4 = [u / n4 for u in st4]
         wb4, kvb4 = decode_bytes(w4, w4.batch, p0 + 1)
@@ -611,46 +716,31 @@ def main():
         torch.cuda.empty_cache()
         log("workload llama2-70b decode, one GPU's share under 8-way tensor parallelism")
         dec4["tp8_share"] = bench_tp_share(dev, flush, max(a.decode_steps, 3))
-        del flush
-        torch.cuda.empty_cache()
-        if not a.no_cpu_baseline:
-            import numpy as np
-            log("cpu oracle: one decode step of each decode workload")
+        if cpu:
+            log("cpu oracle: one decode step of the 70B-shaped workload")
             c4k, c4v = (c.to(torch.float32).numpy() for c in cache)
             dec4["cpu_oracle_step_us"] = round(cpu_decode_step_us(w4, wts4, wl.activations(w4), c4k, c4v, p0), 1)
             dec4["cpu_oracle_note"] = "oracle, numpy float64, one call over the same seeded cache (host cores)"
-            shape3 = (1, S3 + 1, w3.n_kv_heads, w3.head_dim)
-            x3d = wl.activations(w3)[:, S3:S3 + 1].contiguous()
-            dec3["cpu_oracle_step_us"] = round(cpu_decode_step_us(w3, wts3, x3d, np.zeros(shape3), np.zeros(shape3),
-                                                                  S3), 1)
-            dec3["cpu_oracle_note"] = ("oracle, numpy float64, one call at position 8192 over a zero cache of the "
-                                       "same shape (its cost depends on the shape only)")
-        extra.update({"llama3_8b_prefill_8192": pre3, "llama3_8b_decode": dec3, "llama2_70b_decode_b32": dec4})
-
-    if not a.prefill_only:
+        extra["llama2_70b_decode_b32"] = dec4
+    del flush
+    torch.cuda.empty_cache()
+    if "tiny" in sections:
         log("workload tiny-f32: 64-token prefill, then one-token calls")
-        extra["tiny_f32"] = bench_tiny(dev, not a.no_cpu_baseline)
-
-    if a.stack:
-        extra["llama3_8b_stack"] = bench_stack(dev, a.decode_steps)
-        if not a.no_cpu_baseline:
-            log("cpu oracle: bounded sample of the 32-layer stack")
-            extra["llama3_8b_stack"]["cpu_oracle"] = stack_oracle_sample(wl.WORKLOADS[5])
-
-    cpu = None
-    if not a.no_cpu_baseline:
-        log("cpu baseline: oracle on the same workload")
-        cpu = cpu_baseline(w2, wts2, wl.activations(w2))
+        extra["tiny_f32"] = bench_tiny(dev, cpu)
 
     line = {
-        "metric": METRIC, "value": round(tokens / wall, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
-        "warmup": a.warmup, "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
-        "config": {"workload": w2.name, "dim": w2.dim, "n_heads": w2.n_heads, "n_kv_heads": w2.n_kv_heads,
-                   "ffn_hidden": w2.ffn_hidden, "batch": w2.batch, "seq_len": w2.prefill_len,
-                   "parallelism": "none (1 GPU)"},
+        "metric": METRIC, "value": round(value, 1) if value is not None else None, "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(wall * 1e3, 3) if wall is not None else None, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded random token ids, N(0,0.02) weights, unit RMSNorm weights)",
+        "config": {"workload": w5.name, "layers": w5.n_layers, "dim": w5.dim, "n_heads": w5.n_heads,
+                   "n_kv_heads": w5.n_kv_heads, "ffn_hidden": w5.ffn_hidden, "vocab": w5.vocab_size,
+                   "batch": w5.batch, "seq_len": w5.prefill_len, "decode_steps": a.stack_decode_steps,
+                   "value_is": "prefill tokens/s per block = batch x seq_len x layers / prefill step time",
+                   "parallelism": "none (1 GPU)", "sections": sections},
         "roofline": roofline,
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu_base,
         **extra,
     }
     print(json.dumps(line), flush=True)

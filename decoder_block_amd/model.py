@@ -59,17 +59,24 @@ class StackRunner:
         return [b[:n].view(bsz, seqlen, self.args.dim) for b in self.bufs]
 
     def forward(self, tokens: torch.Tensor, start_pos: int, logits: torch.Tensor, next_tok: torch.Tensor,
-                layer_hook=None) -> None:
+                layer_hook=None, layer_events=None) -> None:
         """One call (prefill when tokens has several columns, decode when one):
-        writes the last position's fp32 logits [bsz, vocab] and greedy ids [bsz]."""
+        writes the last position's fp32 logits [bsz, vocab] and greedy ids [bsz].
+        ``layer_events`` (optional): one list of 8 timing events per layer, recorded
+        between the block's stages as llama_block_forward_events describes."""
         bsz, seqlen = tokens.shape
         ws_bytes = self._workspace(bsz, seqlen, start_pos)
         a, b = self._acts(bsz, seqlen)
         D = self.args.dim
         L.llama_embedding(tokens, self.embedding, a, bsz * seqlen, D, self.vocab)
         for i, layer in enumerate(self.layers):
-            L.llama_block_forward(self.args, layer.cw, layer.cache_k, layer.cache_v, layer.freqs, layer.freqs_end,
-                                  a, b, bsz, seqlen, start_pos, self.ws, ws_bytes)
+            if layer_events is not None:
+                L.llama_block_forward_events(self.args, layer.cw, layer.cache_k, layer.cache_v, layer.freqs,
+                                             layer.freqs_end, a, b, bsz, seqlen, start_pos, self.ws, ws_bytes,
+                                             layer_events[i])
+            else:
+                L.llama_block_forward(self.args, layer.cw, layer.cache_k, layer.cache_v, layer.freqs,
+                                      layer.freqs_end, a, b, bsz, seqlen, start_pos, self.ws, ws_bytes)
             if layer_hook is not None:
                 layer_hook(i, a, b)
             a, b = b, a
