@@ -20,6 +20,7 @@ LLAMA_ERR_INVALID_ARG = -1
 LLAMA_ERR_UNSUPPORTED = -2
 LLAMA_ERR_WORKSPACE_TOO_SMALL = -3
 LLAMA_ERR_HIP = -4
+LLAMA_ERR_SCRATCH_TOO_SMALL = -5
 LLAMA_F32 = 0
 LLAMA_BF16 = 1
 
@@ -31,6 +32,7 @@ EXPORTS = (
     "llama_swiglu_ffn", "llama_linear", "llama_block_forward", "llama_block_forward_events",
     "llama_block_decode_at", "llama_embedding",
     "llama_lm_head_workspace_size", "llama_lm_head_argmax", "llama_sample_top_p",
+    "llama_gqa_attn_decode_static", "llama_static_scratch_bytes",
 )
 
 
@@ -109,6 +111,8 @@ def lib() -> ctypes.CDLL:
             "llama_embedding": ([P, P, P, I64, I32, I32, ctypes.c_int, P], ctypes.c_int),
             "llama_lm_head_argmax": ([P, I64, P, P, P, P, I32, I32, I32, F, P, SZ, ctypes.c_int, P], ctypes.c_int),
             "llama_sample_top_p": ([P, P, I32, I32, F, F, P, P], ctypes.c_int),
+            "llama_gqa_attn_decode_static": ([P, P, P, P, P, P, A, I32, I32, ctypes.c_int, P], ctypes.c_int),
+            "llama_static_scratch_bytes": ([], SZ),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -213,6 +217,19 @@ def llama_gqa_attn_decode(xq, xk, xv, cache_k, cache_v, out, args: ModelArgs, bs
     _check(lib().llama_gqa_attn_decode(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(cache_k), _ptr(cache_v), _ptr(out),
                                        ctypes.byref(args.c()), bsz, start_pos, _ptr(ws), ws_bytes, _dtype(xq),
                                        _stream(stream)), "llama_gqa_attn_decode")
+
+
+def llama_gqa_attn_decode_static(xq, xk, xv, cache_k, cache_v, out, args: ModelArgs, bsz: int, start_pos: int,
+                                 stream=None) -> None:
+    """llama_gqa_attn_decode without a workspace: the partials go to the library's static
+    per-GPU scratch array (no allocation on the call)."""
+    _check(lib().llama_gqa_attn_decode_static(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(cache_k), _ptr(cache_v),
+                                              _ptr(out), ctypes.byref(args.c()), bsz, start_pos, _dtype(xq),
+                                              _stream(stream)), "llama_gqa_attn_decode_static")
+
+
+def llama_static_scratch_bytes() -> int:
+    return int(lib().llama_static_scratch_bytes())
 
 
 def llama_swiglu_ffn(x, w1, w3, w2, y, rows: int, dim: int, hidden: int, ws, ws_bytes: int, stream=None) -> None:

@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "attention.hpp"
 #include "gemm.hpp"
@@ -229,6 +230,7 @@ const char* llama_status_str(int s) {
     case LLAMA_ERR_UNSUPPORTED: return "unsupported dtype/head_dim combination";
     case LLAMA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case LLAMA_ERR_HIP: return "HIP launch error";
+    case LLAMA_ERR_SCRATCH_TOO_SMALL: return "the call needs more than the library's static scratch holds";
     default: return "unknown status";
   }
 }
@@ -354,9 +356,12 @@ int llama_gqa_attn_prefill(const void* xq, const void* xk, const void* xv, void*
   return hip_status(e);
 }
 
-int llama_gqa_attn_decode(const void* xq, const void* xk, const void* xv, void* cache_k, void* cache_v, void* out,
-                          const llama_model_args* a, int32_t bsz, int32_t start_pos, void* ws, size_t ws_bytes,
-                          llama_dtype dt, llama_stream_t stream) {
+// Validation and launch shared by llama_gqa_attn_decode and its allocation-free
+// variant; `partial` is the split-K buffer (at least `need` bytes, reported
+// through need_out before any launch so the caller can bound it).
+static int attn_decode_impl(const void* xq, const void* xk, const void* xv, void* cache_k, void* cache_v, void* out,
+                            const llama_model_args* a, int32_t bsz, int32_t start_pos, void* ws, size_t ws_bytes,
+                            llama_dtype dt, llama_stream_t stream, bool static_ws) {
   Dims g;
   int rc = model_dims(a, dt, &g);
   if (rc != LLAMA_OK) return rc;
@@ -364,9 +369,9 @@ int llama_gqa_attn_decode(const void* xq, const void* xk, const void* xv, void* 
   if (rc != LLAMA_OK) return rc;
   if (!xq || !xk || !xv || !cache_k || !cache_v || !out) return LLAMA_ERR_INVALID_ARG;
   const size_t need = decode_partial_floats(g, bsz, start_pos + 1, dt) * sizeof(float);
-  if (need && !ws) return LLAMA_ERR_INVALID_ARG;
+  if (need && !ws) return static_ws ? LLAMA_ERR_HIP : LLAMA_ERR_INVALID_ARG;
   if (!all_al16(xq, xk, xv, cache_k, cache_v, out, need ? ws : nullptr)) return LLAMA_ERR_INVALID_ARG;
-  if (ws_bytes < need) return LLAMA_ERR_WORKSPACE_TOO_SMALL;
+  if (ws_bytes < need) return static_ws ? LLAMA_ERR_SCRATCH_TOO_SMALL : LLAMA_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = (hipStream_t)stream;
   llama::AttnShape sh{bsz, 1, start_pos, g.H, g.Hkv, g.d, a->max_seq_len};
   hipError_t e;
@@ -382,6 +387,64 @@ int llama_gqa_attn_decode(const void* xq, const void* xk, const void* xv, void* 
                                     (float*)ws, st);
   }
   return hip_status(e);
+}
+
+int llama_gqa_attn_decode(const void* xq, const void* xk, const void* xv, void* cache_k, void* cache_v, void* out,
+                          const llama_model_args* a, int32_t bsz, int32_t start_pos, void* ws, size_t ws_bytes,
+                          llama_dtype dt, llama_stream_t stream) {
+  return attn_decode_impl(xq, xk, xv, cache_k, cache_v, out, a, bsz, start_pos, ws, ws_bytes, dt, stream, false);
+}
+
+// Allocation-free decode attention: the split-K partials live in `scratch`, one
+// copy per GPU (a file-scope device array, so the library never calls hipMalloc).
+// On the first call on a device its address is fetched with hipGetSymbolAddress
+// (the array's name is only a host-side stand-in, not a device address) and kept
+// per device; kernels receive that address.  Nothing in the partials has to start
+// at zero: every split writes all of its (max, sum, o) entries before the merge
+// kernel reads them.
+}  // extern "C"
+
+namespace {
+// 8 MiB: the split rule gives at most about 4 MiB of partials below four million
+// attended keys (at most 512 splits x 16 query heads per kv head), 8.1 MiB beyond
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this GPU's scratch array, or nullptr on a HIP error.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+size_t llama_static_scratch_bytes(void) { return kScratchBytes; }
+
+int llama_gqa_attn_decode_static(const void* xq, const void* xk, const void* xv, void* cache_k, void* cache_v,
+                                 void* out, const llama_model_args* a, int32_t bsz, int32_t start_pos, llama_dtype dt,
+                                 llama_stream_t stream) {
+  // the size check comes first, on the host, so an oversized call never touches the device
+  Dims g;
+  int rc = model_dims(a, dt, &g);
+  if (rc != LLAMA_OK) return rc;
+  rc = call_shape(a, bsz, 1, start_pos);
+  if (rc != LLAMA_OK) return rc;
+  const size_t need = decode_partial_floats(g, bsz, start_pos + 1, dt) * sizeof(float);
+  if (need > kScratchBytes) return LLAMA_ERR_SCRATCH_TOO_SMALL;
+  void* ws = need ? scratch_on_current_device() : nullptr;
+  if (need && !ws) return LLAMA_ERR_HIP;
+  return attn_decode_impl(xq, xk, xv, cache_k, cache_v, out, a, bsz, start_pos, ws, kScratchBytes, dt, stream, true);
 }
 
 int llama_linear(const void* x, const void* w, void* y, int64_t rows, int32_t in, int32_t outf, llama_dtype dt,

@@ -53,7 +53,8 @@ enum {
   LLAMA_ERR_INVALID_ARG = -1,        /* null pointer, bad size or inconsistent shape */
   LLAMA_ERR_UNSUPPORTED = -2,        /* valid but not built: dtype/head_dim combination */
   LLAMA_ERR_WORKSPACE_TOO_SMALL = -3,/* ws_bytes below the size the *_workspace_size call reports */
-  LLAMA_ERR_HIP = -4                 /* a HIP launch reported an error */
+  LLAMA_ERR_HIP = -4,                /* a HIP launch reported an error */
+  LLAMA_ERR_SCRATCH_TOO_SMALL = -5   /* an allocation-free call needs more than its static scratch */
 };
 
 typedef enum { LLAMA_F32 = 0, LLAMA_BF16 = 1 } llama_dtype;
@@ -173,6 +174,30 @@ int llama_gqa_attn_decode(const void* xq, const void* xk, const void* xv, void* 
                           void* cache_v, void* out, const llama_model_args* args, int32_t bsz,
                           int32_t start_pos, void* ws, size_t ws_bytes, llama_dtype dtype,
                           llama_stream_t stream);
+
+/* Allocation-free variant of llama_gqa_attn_decode, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation, kernels and results,
+ * with the split-K partials in a static device array of the library instead of
+ * a caller workspace.  Each GPU holds its own copy of the array (8 MiB, see
+ * llama_static_scratch_bytes) from the first call on that device until the
+ * process ends; the call makes no hipMalloc/hipFree and allocates nothing else.
+ * Call it with the device of `stream` current (its scratch address is looked up
+ * for the current device).  A call whose partials
+ * (bsz * n_heads * splits * (head_dim + 2) floats, the same count as
+ * llama_attn_decode_workspace_size reports) exceed the array returns
+ * LLAMA_ERR_SCRATCH_TOO_SMALL before anything is enqueued.  Every call on one
+ * GPU shares that GPU's array and nothing in it needs clearing between calls;
+ * calls that can overlap on one GPU (different streams) race on it and must be
+ * ordered by the caller.  Arguments, layouts and other errors as
+ * llama_gqa_attn_decode. */
+int llama_gqa_attn_decode_static(const void* xq, const void* xk, const void* xv, void* cache_k,
+                                 void* cache_v, void* out, const llama_model_args* args,
+                                 int32_t bsz, int32_t start_pos, llama_dtype dtype,
+                                 llama_stream_t stream);
+
+/* Size in bytes of the static scratch array behind llama_gqa_attn_decode_static.  Host only. */
+size_t llama_static_scratch_bytes(void);
 
 /* SwiGLU feed-forward without residual (notes, section 3, FeedForward.forward):
  * y = w2( silu(w1 x) * (w3 x) ), silu(a) = a / (1 + e^-a).

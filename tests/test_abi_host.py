@@ -274,3 +274,21 @@ def test_binding_checks_tensor_extents_before_the_call():
         dba.llama_block_forward(a, wts, ck, cv, 1 << 20, 16, x, out[:1], 2, 4, 0, 1 << 20, 0)
     with pytest.raises(ValueError, match="x"):
         dba.llama_block_decode_at(a, wts, ck, cv, 1 << 20, 16, x[:, :1][:1], out, 2, 1 << 20, 3, 1 << 20, 0)
+
+
+def test_static_scratch_decode_refuses_oversized_calls_on_the_host():
+    """llama_gqa_attn_decode_static keeps its split-K partials in an 8 MiB static
+    array: a call whose partials need more (one sequence, 16 query heads on one kv
+    head, 4.2 million attended keys: 8.08 MiB) is refused before anything reaches
+    the device; the size check precedes the scratch lookup and every launch."""
+    lib = dba.lib()
+    assert lib.llama_static_scratch_bytes() == 8 << 20
+    a = dba.ModelArgs(dim=2048, n_heads=16, n_kv_heads=1, multiple_of=256, max_batch_size=1, max_seq_len=4_200_001)
+    assert dba.llama_attn_decode_workspace_size(a, 1, 4_200_000) > lib.llama_static_scratch_bytes()
+    p = 1 << 20
+    assert lib.llama_gqa_attn_decode_static(p, p, p, p, p, p, ctypes.byref(a.c()), 1, 4_200_000, dba.LLAMA_BF16,
+                                            None) == dba._lib.LLAMA_ERR_SCRATCH_TOO_SMALL
+    # argument errors come back as for the workspace call
+    assert lib.llama_gqa_attn_decode_static(p, p, p, p, p, p, ctypes.byref(a.c()), 2, 10, dba.LLAMA_BF16,
+                                            None) == dba._lib.LLAMA_ERR_INVALID_ARG
+    assert "scratch" in dba.status_str(dba._lib.LLAMA_ERR_SCRATCH_TOO_SMALL)
