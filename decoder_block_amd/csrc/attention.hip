@@ -154,8 +154,10 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
   constexpr int KPB = 1024 / (HD * 2);        // key rows per 1 KiB DMA block
   constexpr int DMA = BKV / KPB / 4;          // DMA instructions per wave per tensor per tile
   static_assert(HD == 64 || HD == 128, "head_dim");
-  __shared__ bf16x8 Ks[2][BKV * CHK];
-  __shared__ bf16x8 Vs[2][BKV * CHK];
+  // one array per ring slot: the waitcnt pass then sees that reads of one slot
+  // cannot alias the DMA into the other, and does not drain the prefetch first
+  __shared__ bf16x8 Ks0[BKV * CHK], Ks1[BKV * CHK];
+  __shared__ bf16x8 Vs0[BKV * CHK], Vs1[BKV * CHK];
   // bank-group swizzles: K rows are read 16 keys at a time (one chunk), V rows 4 keys x 32 bytes
   auto kswz = [](int key) { return CHK == 16 ? (key & 15) : ((key >> 1) & 7); };
   auto vswz = [](int key) { return CHK == 16 ? ((key & 3) << 2) : (((key >> 1) & 1) << 2); };
@@ -227,9 +229,9 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
       const int t = full ? t0 + dkey[i] : min(t0 + dkey[i], kend - 1);
       const uint32_t row = (uint32_t)t * stride_b;
       __builtin_amdgcn_global_load_lds((const void*)(kb8 + (row + dk_off[i])),
-                                       (LLAMA_LDS void*)&Ks[ST][(wave * DMA + i) * 64], 16, 0, 0);
+                                       (LLAMA_LDS void*)&(ST ? Ks1 : Ks0)[(wave * DMA + i) * 64], 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)(vb8 + (row + dv_off[i])),
-                                       (LLAMA_LDS void*)&Vs[ST][(wave * DMA + i) * 64], 16, 0, 0);
+                                       (LLAMA_LDS void*)&(ST ? Vs1 : Vs0)[(wave * DMA + i) * 64], 16, 0, 0);
     }
   };
 
@@ -241,21 +243,21 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
   // sub-tile and the second 8 keys of a V^T read are immediate offsets.  The
   // swizzles depend only on the key's low bits, which the sub-tile offsets
   // (multiples of 8 keys) leave unchanged.
-  const bf16x8* kfp[HD / 16];
+  int kfo[HD / 16];
 #pragma unroll
   for (int kk = 0; kk < HD / 16; ++kk) {
     const int c = kk * 2 + lhalf;
-    kfp[kk] = &Ks[0][lrow * CHK + (c ^ kswz(lrow))];
+    kfo[kk] = lrow * CHK + (c ^ kswz(lrow));
   }
   // V^T read: lane group g = lane/16 covers d0 = (g&1)*16 (+32*dt), keys base + hf*4 (+8)
   const int li = lane & 15;
   const int vkey_off = lhalf * 4 + (li >> 2);
   const int vd_off = ((lane >> 4) & 1) * 16 + (li & 3) * 4;
-  const bf16* vtp[HD / 32];
+  int vto[HD / 32];                           // element offsets into a V slot
 #pragma unroll
   for (int dt = 0; dt < HD / 32; ++dt) {
     const int d = dt * 32 + vd_off;
-    vtp[dt] = (const bf16*)&Vs[0][vkey_off * CHK + ((d >> 3) ^ vswz(vkey_off))] + (d & 7);
+    vto[dt] = (vkey_off * CHK + ((d >> 3) ^ vswz(vkey_off))) * 8 + (d & 7);
   }
 
   auto tile = [&](int it, auto st_c) {
@@ -266,15 +268,31 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
     asm volatile("" ::: "memory");
     if (it + 1 < ntiles) issue(t0 + BKV, std::integral_constant<int, ST ^ 1>{});
 
+    // S^T = K.Q^T: the K fragment reads run AHEAD reads in front of the MFMAs
+    // that consume them (left to itself the compiler kept one or two reads in
+    // flight, so each MFMA waited out a whole LDS latency)
+    constexpr int NKF = 2 * (HD / 16);        // K fragments per tile
+    constexpr int AHEAD = HD / 16;
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    bf16x8 kf[2][HD / 16];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int kk = 0; kk < HD / 16; ++kk) {
-        const bf16x8 kf = kfp[kk][ST * BKV * CHK + kt * 32 * CHK];
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[kt], 0, 0, 0);
-      }
+      for (int kk = 0; kk < HD / 16; ++kk) kf[kt][kk] = (ST ? Ks1 : Ks0)[kfo[kk] + kt * 32 * CHK];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int kk = 0; kk < HD / 16; ++kk)
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kt][kk], qf[kk], sacc[kt], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+    for (int i = 0; i < NKF - AHEAD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+    __builtin_amdgcn_sched_barrier(0);
     // causal mask only where this wave's rows meet the diagonal
     if (t0 + BKV - 1 > wave_qmin) {
 #pragma unroll
@@ -321,7 +339,7 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
       for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
         for (int dt = 0; dt < HD / 32; ++dt) {
-          const bf16* v1 = vtp[dt] + (ST * BKV + kt * 32 + h2 * 16) * CHK * 8;
+          const bf16* v1 = (const bf16*)(ST ? Vs1 : Vs0) + vto[dt] + (kt * 32 + h2 * 16) * CHK * 8;
           const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LLAMA_LDS bf16x4_t*)v1);
           const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LLAMA_LDS bf16x4_t*)(v1 + 8 * CHK * 8));
           const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
