@@ -219,26 +219,31 @@ def test_stack_graph_decode_replays_match_eager(host_weights, temperature):
     torch.cuda.empty_cache()
 
 
-def test_stack_decode_paths_agree_layer_by_layer(host_weights):
-    """One batch-64 decode step through both one-token entry points on identical
-    per-layer inputs: llama_block_forward (position passed by the host, attention
-    split by the actual length) and llama_block_decode_at (position read on the
-    device, splits laid out for a larger bound, so the fp32 sums run in another
-    order).  Layer l's input is the host-position path's output of layer l - 1;
-    both outputs of every layer, the appended cache rows and the final logits
-    must agree within the bf16 tolerance."""
+@pytest.mark.parametrize("B,bound", [(64, 128 + 255), (4, 2200)])
+def test_stack_decode_paths_agree_layer_by_layer(host_weights, B, bound):
+    """One decode step through both one-token entry points on identical per-layer
+    inputs: llama_block_forward (position passed by the host, attention split by
+    the actual length) and llama_block_decode_at (position read on the device,
+    splits laid out for the bound).  At batch 64 both take one split per
+    (sequence, kv group) and must agree bit for bit; at batch 4 the bound of 2200
+    positions lays out 14 splits where the host path uses 2, so the fp32 sums run
+    in another order (and the projections take the one-to-four-token weight
+    streams).  Layer l's input is the host-position path's output of layer l - 1;
+    the outputs of every layer and the appended k rows must agree within the bf16
+    tolerance."""
     dev = need_gpu()
     layers, emb, norm_w, w_out = host_weights
     w = W5
-    S, bound = 128, 128 + 255
-    print(f"case {w.name}: decode step at {S} through both one-token entry points, B={w.batch}", flush=True)
-    args = model_args_for(w, max_seq=bound + 1)
+    S = 128
+    print(f"case {w.name}: decode step at {S} through both one-token entry points, B={B}, bound {bound}",
+          flush=True)
+    args = model_args_for(w, max_batch=B, max_seq=bound + 1)
     stack = StackRunner(args, lambda l: layers[l], emb, norm_w, w_out, torch.bfloat16, dev)
-    prompt = wl.prompt_tokens(w)[:, :S].contiguous().to(dev)
-    logits = torch.empty(w.batch, w.vocab_size, dtype=torch.float32, device=dev)
-    tok = torch.empty(w.batch, dtype=torch.int32, device=dev)
+    prompt = wl.prompt_tokens(w)[:B, :S].contiguous().to(dev)
+    logits = torch.empty(B, w.vocab_size, dtype=torch.float32, device=dev)
+    tok = torch.empty(B, dtype=torch.int32, device=dev)
     stack.forward(prompt, 0, logits, tok)
-    B, D = w.batch, w.dim
+    D = w.dim
     need = max(L.llama_block_workspace_size(args, B, 1, bound, L.LLAMA_BF16),
                L.llama_block_workspace_size(args, B, 1, S, L.LLAMA_BF16))
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -256,6 +261,8 @@ def test_stack_decode_paths_agree_layer_by_layer(host_weights):
         torch.cuda.synchronize()
         e = check(b, f64(a), "bf16", f"layer {l}: device-position vs host-position output")
         assert torch.equal(ka, r.cache_k[:, S]), f"layer {l}: the two paths appended different k rows"
+        if B == 64:
+            assert torch.equal(a, b), f"layer {l}: one split each, yet the outputs differ"
         worst = max(worst, e["relf"])
         h = a
     print(f"[paths] worst per-layer relF between the two one-token paths {worst:.3e}", flush=True)
