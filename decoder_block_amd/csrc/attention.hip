@@ -439,6 +439,11 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
   // through a per-wave LDS tile into that layout.  The swizzle ksw keeps both
   // the row writes and the 16-key operand reads free of bank conflicts.
   auto ksw = [](int r) { return HD == 128 ? (r & 15) : ((r >> 1) & 7); };
+  // V tile slot of (dim d, key group kg): the four slots of each dim, XOR-ed
+  // within their 16-slot block by d / 4, so that the operand reads (16 dims of
+  // one key group) hit 16 different bank groups and the transposed writes (16
+  // dims 8 apart) at most two lanes per bank group.
+  auto vsw = [](int d, int kg) { return (d * 4 + kg) ^ ((d >> 2) & 15); };
   const int rstride = (int)stride;
   auto load = [&](int c0, bf16x8 (&kr)[KL], bf16x8 (&vk)[8]) {
 #pragma unroll
@@ -465,7 +470,7 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
       for (int dd = 0; dd < 8; ++dd) {
         const int d = vdc * 8 + dd;
         bf16x8 w = {vk[0][dd], vk[1][dd], vk[2][dd], vk[3][dd], vk[4][dd], vk[5][dd], vk[6][dd], vk[7][dd]};
-        Vt[wave][d * 4 + (vg ^ ((d >> 2) & 3))] = w;
+        Vt[wave][vsw(d, vg)] = w;
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -519,7 +524,7 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
 #pragma unroll
     for (int dt = 0; dt < HD / 16; ++dt) {
       const int d = dt * 16 + l16;
-      bf16x8 vf = Vt[wave][d * 4 + (g ^ ((d >> 2) & 3))];
+      bf16x8 vf = Vt[wave][vsw(d, g)];
       oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[dt], 0, 0, 0);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
