@@ -180,7 +180,8 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
   const int h0 = hg * G;
   const int j = h0 / n_rep;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar LDS bases and branches
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int R = wave * 32 + lrow;
   const int s = qb * BQ + R % BQ;
@@ -218,20 +219,28 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
   for (int i = 0; i < DMA; ++i) {
     const int key = (wave * DMA + i) * KPB + lane / CHK;
     dkey[i] = key;
-    dk_off[i] = (uint32_t)(((lane % CHK) ^ kswz(key)) * 16);
-    dv_off[i] = (uint32_t)(((lane % CHK) ^ vswz(key)) * 16);
+    // byte offset of the lane's chunk in the tile's first row block (a tile adds t0 rows)
+    dk_off[i] = (uint32_t)key * stride_b + (uint32_t)(((lane % CHK) ^ kswz(key)) * 16);
+    dv_off[i] = (uint32_t)key * stride_b + (uint32_t)(((lane % CHK) ^ vswz(key)) * 16);
   }
   auto issue = [&](int t0, auto st_c) {
     constexpr int ST = decltype(st_c)::value;
-    const bool full = t0 + BKV <= kend;          // no key of the tile past the end: no clamp
+    auto copy = [&](int i, uint32_t ko, uint32_t vo) {
+      __builtin_amdgcn_global_load_lds((const void*)(kb8 + ko), (LLAMA_LDS void*)&(ST ? Ks1 : Ks0)[(wave * DMA + i) * 64],
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vb8 + vo), (LLAMA_LDS void*)&(ST ? Vs1 : Vs0)[(wave * DMA + i) * 64],
+                                       16, 0, 0);
+    };
+    if (t0 + BKV <= kend) {                      // no key of the tile past the end: no clamp
+      const uint32_t tb = (uint32_t)t0 * stride_b;
 #pragma unroll
-    for (int i = 0; i < DMA; ++i) {
-      const int t = full ? t0 + dkey[i] : min(t0 + dkey[i], kend - 1);
-      const uint32_t row = (uint32_t)t * stride_b;
-      __builtin_amdgcn_global_load_lds((const void*)(kb8 + (row + dk_off[i])),
-                                       (LLAMA_LDS void*)&(ST ? Ks1 : Ks0)[(wave * DMA + i) * 64], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vb8 + (row + dv_off[i])),
-                                       (LLAMA_LDS void*)&(ST ? Vs1 : Vs0)[(wave * DMA + i) * 64], 16, 0, 0);
+      for (int i = 0; i < DMA; ++i) copy(i, dk_off[i] + tb, dv_off[i] + tb);
+    } else {
+#pragma unroll
+      for (int i = 0; i < DMA; ++i) {
+        const uint32_t tb = (uint32_t)(min(t0 + dkey[i], kend - 1) - dkey[i]) * stride_b;
+        copy(i, dk_off[i] + tb, dv_off[i] + tb);
+      }
     }
   };
 
@@ -320,16 +329,25 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
       for (int dt = 0; dt < HD / 32; ++dt) oacc[dt] *= alpha;
       m_run = m_new;
     }
-    float psum = 0.f;
     bf16x8 pf[2][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][v], scale_log2, -m_run));
-        psum += p;
-        pf[kt][v >> 3][v & 7] = (bf16)p;
-      }
+      for (int v = 0; v < 16; ++v)
+        pf[kt][v >> 3][v & 7] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][v], scale_log2, -m_run));
+    // the row sum of the probabilities exactly as P.V uses them (bf16), two per dot2
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x2 pp = {pf[kt][h2][2 * j], pf[kt][h2][2 * j + 1]};
+          ps[j] = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, ps[j], false);
+        }
+    float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
     psum += __shfl_xor(psum, 32, 64);
     l_run += psum;
 
