@@ -317,7 +317,7 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mraw = fmaxf(mraw, sacc[kt][v]);
-    mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+    mraw = pair_max32(mraw);
     const float mt = mraw * scale_log2;       // tile max in the log2 domain (scale > 0)
     // lazy rescale: the running max moves only when some row's max grows by more
     // than 8 (probabilities then stay below 2^8); the result is unchanged
@@ -348,7 +348,7 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
           ps[j] = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, ps[j], false);
         }
     float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    psum += __shfl_xor(psum, 32, 64);
+    psum = pair_sum32(psum);
     l_run += psum;
 
 #pragma unroll
@@ -514,8 +514,7 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
         sacc[kt][v] = x;
         mloc = fmaxf(mloc, x);
       }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    mloc = pair_max32(pair_max16(mloc));
     // lazy rescale: the running max moves only when some head's max grows by
     // more than 8 (probabilities then stay below 2^8); the result is unchanged
     if (__any(mloc > m_run + 8.0f)) {
@@ -536,8 +535,7 @@ attn_decode_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const 
         psum += p;
         pf[kt * 4 + v] = (bf16)p;
       }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
+    psum = pair_sum32(pair_sum16(psum));
     l_run += psum;
 #pragma unroll
     for (int dt = 0; dt < HD / 16; ++dt) {

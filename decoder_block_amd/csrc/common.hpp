@@ -56,6 +56,28 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Reductions over lane pairs (l, l ^ 16) and (l, l ^ 32) with the gfx950 lane
+// swaps: each returns op(v[l], v[l ^ off]) on every lane, from VALU
+// instructions instead of an LDS permute.  A swap of v with itself leaves, in
+// its two results, v[l] and v[l ^ off] (in an order that depends on the lane),
+// and both ops are symmetric, so every lane of a pair gets the same value.
+__device__ __forceinline__ float pair_max16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_max32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_sum32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Workgroup id remapping so that consecutive logical tiles land on the same
 // XCD (the dispatcher deals workgroups round-robin over the 8 XCDs, each with
 // its own L2).  Identity when the grid is not a multiple of 8.

@@ -1,6 +1,7 @@
 // Projection GEMMs C[m][n] = sum_k A[m][k] W[n][k] for gfx950.
 //
-// bf16: LDS-staged, double-buffered tiles feeding v_mfma_f32_32x32x16_bf16.
+// bf16: LDS-staged, double-buffered tiles feeding v_mfma_f32_16x16x32_bf16
+// (large tiles) or v_mfma_f32_32x32x16_bf16 (decode-sized tiles).
 // The weight tile is the MFMA "A" operand (rows i = n) and the activation tile
 // the "B" operand (columns j = m), so each lane's accumulators hold four
 // consecutive output columns n of one token row m: the epilogue can rotate
@@ -14,6 +15,8 @@
 // bound), same epilogues.
 #include "gemm.hpp"
 
+#include <type_traits>
+
 namespace llama {
 
 namespace {
@@ -24,6 +27,13 @@ constexpr int kThreads = 256;
 constexpr int kBigBK = 64;
 constexpr int kBigStages = 2;
 constexpr int kBigWaves = 8;
+// MFMA shape of the large tiles: 16x16x32.  Per flop it reads and writes half
+// the accumulator registers of 32x32x16 for the same LDS fragment bytes (a
+// 128 x 64 wave tile reads 192 rows of k either way); measured on the
+// Llama-3-8B-shaped block (M = 8192) it ran the dual w1/w3 GEMM at 1.32-1.34
+// instead of 1.24-1.25 PF/s, w2 1.34-1.35 instead of 1.24-1.25, QKV and wo 8-9 %
+// faster, at the same LDS traffic and the same number of waves.
+constexpr int kBigMI = 16;
 constexpr int kCUs = 256;         // MI355X compute units
 // small M (<= 64 tokens: the weights stream from HBM once): 64-deep k-tiles
 // (128-byte row pieces).  Tiles: M <= 32: 32 rows x 128 columns, 32 x 256 for
@@ -161,6 +171,10 @@ gemm_bf16_mfma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int 
   __syncthreads();
 
   const int lrow = lane & 31, lhalf = lane >> 5;
+  // (the epilogue below is shared in form with the DMA kernel's)
+  constexpr int MI = 32, NV = 4;
+  using acc_t = f32x16;
+  const int lk = lhalf;
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < nk) gload(kb + (kt + 1) * BK);
@@ -191,17 +205,17 @@ gemm_bf16_mfma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int 
   // epilogue: lane holds n = base + g*8 + lhalf*4 + {0..3} of row m = .. + lrow
 #pragma unroll
   for (int b = 0; b < TM; ++b) {
-    const int m = m0 + wm * WM + b * 32 + lrow;
+    const int m = m0 + wm * WM + b * MI + lrow;
     if (m >= M) continue;
     if constexpr (DUAL) {
 #pragma unroll
       for (int a = 0; a < TN / 2; ++a)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * (WN / 2) + a * 32 + g * 8 + lhalf * 4;
+        for (int g = 0; g < NV; ++g) {
+          const int n = n0 + wn * (WN / 2) + a * MI + g * 8 + lk * 4;
           if (n >= N) continue;
           f32x4 v1 = {acc[a][b][g * 4], acc[a][b][g * 4 + 1], acc[a][b][g * 4 + 2], acc[a][b][g * 4 + 3]};
-          const f32x16& a3 = acc[a + TN / 2][b];
+          const acc_t& a3 = acc[a + TN / 2][b];
           f32x4 v3 = {a3[g * 4], a3[g * 4 + 1], a3[g * 4 + 2], a3[g * 4 + 3]};
           if (SPLIT) {
             float* p = partial + ((int64_t)blockIdx.z * M + m) * (2 * (int64_t)N);
@@ -254,7 +268,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(63 | (7 << 4) | (0 << 8) | (3 << 14)); }
 
-template <int BM, int BN, int BK, int WAVES_M, int NS, bool DUAL, bool SPLIT, class Epi, int NW>
+template <int BM, int BN, int BK, int WAVES_M, int NS, bool DUAL, bool SPLIT, class Epi, int NW, int MI>
 __global__ void __launch_bounds__(NW * 64)
 gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M, int N, int K, int k_per_split,
               Epi epi, float* __restrict__ partial) {
@@ -262,13 +276,20 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
   constexpr int RPB = 64 / CH;                // tile rows per 1 KiB DMA block
   constexpr int WAVES_N = NW / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-  constexpr int TM = WM / 32, TN = WN / 32;
+  // MFMA shape: MI x MI outputs, KM deep (32x32x16 or 16x16x32); a fragment is
+  // MI rows x KM k, lane l holding 8 consecutive k of row l % MI (k block l / MI)
+  constexpr int KM = MI == 32 ? 16 : 32;
+  constexpr int LG = 64 / MI;                 // k blocks of 8 per fragment
+  constexpr int NV = MI == 32 ? 4 : 1;        // groups of 4 consecutive rows per accumulator
+  using acc_t = typename std::conditional<MI == 32, f32x16, f32x4>::type;
+  static_assert(MI == 32 || MI == 16, "MFMA shape");
+  constexpr int TM = WM / MI, TN = WN / MI;
   constexpr int ROWS = BM + BN;               // rows x 2*BK bytes per stage
   constexpr int BLOCKS = ROWS / RPB;          // 1 KiB DMA blocks per stage
   constexpr int LOADS = BLOCKS / NW;          // per wave (and per lane) per stage
   constexpr int BN_OUT = DUAL ? BN / 2 : BN;
-  constexpr int RD = TN + TM;                 // fragment reads per 16-deep half
-  constexpr int MF = TN * TM;                 // MFMAs per half
+  constexpr int RD = TN + TM;                 // fragment reads per KM-deep step
+  constexpr int MF = TN * TM;                 // MFMAs per step
   static_assert(BK == 32 || BK == 64, "BK");
   static_assert(NS >= 2 && BLOCKS % NW == 0 && TM >= 1 && TN >= 1 && (!DUAL || TN % 2 == 0), "shape");
   static_assert(WAVES_M * WAVES_N == NW, "waves");
@@ -339,12 +360,12 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
     }
   };
   auto wrow = [&](int t) {
-    if (DUAL) return t < TN / 2 ? wn * (WN / 2) + t * 32 : BN / 2 + wn * (WN / 2) + (t - TN / 2) * 32;
-    return wn * WN + t * 32;
+    if (DUAL) return t < TN / 2 ? wn * (WN / 2) + t * MI : BN / 2 + wn * (WN / 2) + (t - TN / 2) * MI;
+    return wn * WN + t * MI;
   };
-  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int lrow = lane % MI, lk = lane / MI;
   auto read_half = [&](int st, int kk, bf16x8* fa, bf16x8* fb) {
-    const int c = kk * 2 + lhalf;
+    const int c = kk * LG + lk;
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       const int r = BM + wrow(t) + lrow;
@@ -352,22 +373,26 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
     }
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
-      const int r = wm * WM + t * 32 + lrow;
+      const int r = wm * WM + t * MI + lrow;
       fb[t] = smem[st][r * CH + (c ^ swz(r))];
     }
   };
 
-  f32x16 acc[TN][TM];
+  acc_t acc[TN][TM];
 #pragma unroll
   for (int a = 0; a < TN; ++a)
 #pragma unroll
-    for (int b = 0; b < TM; ++b) acc[a][b] = f32x16{};
+    for (int b = 0; b < TM; ++b) acc[a][b] = acc_t{};
   auto mfma_half = [&](const bf16x8* fa, const bf16x8* fb) {
 #pragma unroll
     for (int a = 0; a < TN; ++a)
 #pragma unroll
-      for (int b = 0; b < TM; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+      for (int b = 0; b < TM; ++b) {
+        if constexpr (MI == 32)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+        else
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+      }
   };
   // the RD fragment reads for the next step go out one after each of the first
   // MFMAs, leaving the last MF - RD MFMAs (if any) to cover their latency
@@ -379,7 +404,7 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
     }
   };
 
-  constexpr int KS = BK / 16;                 // 16-deep MFMA steps per k-tile
+  constexpr int KS = BK / KM;                 // MFMA steps per k-tile
   bf16x8 fa[2][TN], fb[2][TM];
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) issue(s);
@@ -423,19 +448,21 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
   // no DMA may still be writing LDS when the workgroup retires
   wait_vmcnt<0>();
 
+  // accumulator element g*4 + i of acc[a][b] is output row m = (b * MI + lrow)
+  // and column n = a * MI + g * 8 + lk * 4 + i of the wave's tile
 #pragma unroll
   for (int b = 0; b < TM; ++b) {
-    const int m = m0 + wm * WM + b * 32 + lrow;
+    const int m = m0 + wm * WM + b * MI + lrow;
     if (m >= M) continue;
     if constexpr (DUAL) {
 #pragma unroll
       for (int a = 0; a < TN / 2; ++a)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * (WN / 2) + a * 32 + g * 8 + lhalf * 4;
+        for (int g = 0; g < NV; ++g) {
+          const int n = n0 + wn * (WN / 2) + a * MI + g * 8 + lk * 4;
           if (n >= N) continue;
           f32x4 v1 = {acc[a][b][g * 4], acc[a][b][g * 4 + 1], acc[a][b][g * 4 + 2], acc[a][b][g * 4 + 3]};
-          const f32x16& a3 = acc[a + TN / 2][b];
+          const acc_t& a3 = acc[a + TN / 2][b];
           f32x4 v3 = {a3[g * 4], a3[g * 4 + 1], a3[g * 4 + 2], a3[g * 4 + 3]};
           if (SPLIT) {
             float* p = partial + ((int64_t)blockIdx.z * M + m) * (2 * (int64_t)N);
@@ -449,8 +476,8 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
 #pragma unroll
       for (int a = 0; a < TN; ++a)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * WN + a * 32 + g * 8 + lhalf * 4;
+        for (int g = 0; g < NV; ++g) {
+          const int n = n0 + wn * WN + a * MI + g * 8 + lk * 4;
           if (n >= N) continue;
           f32x4 v = {acc[a][b][g * 4], acc[a][b][g * 4 + 1], acc[a][b][g * 4 + 2], acc[a][b][g * 4 + 3]};
           *(f32x4*)(partial + ((int64_t)blockIdx.z * M + m) * (int64_t)N + n) = v;
@@ -458,19 +485,19 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
     } else {
       // row-dependent parts once, then the fragment's epilogue loads, then its stores
       const auto row = epi_row(epi, m);
-      decltype(epi_pre(epi, row, 0)) pre[TN][4];
+      decltype(epi_pre(epi, row, 0)) pre[TN][NV];
 #pragma unroll
       for (int a = 0; a < TN; ++a)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * WN + a * 32 + g * 8 + lhalf * 4;
+        for (int g = 0; g < NV; ++g) {
+          const int n = n0 + wn * WN + a * MI + g * 8 + lk * 4;
           pre[a][g] = epi_pre(epi, row, min(n, N - 4));
         }
 #pragma unroll
       for (int a = 0; a < TN; ++a)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * WN + a * 32 + g * 8 + lhalf * 4;
+        for (int g = 0; g < NV; ++g) {
+          const int n = n0 + wn * WN + a * MI + g * 8 + lk * 4;
           if (n >= N) continue;
           f32x4 v = {acc[a][b][g * 4], acc[a][b][g * 4 + 1], acc[a][b][g * 4 + 2], acc[a][b][g * 4 + 3]};
           epi_apply(epi, row, n, v, pre[a][g]);
@@ -675,7 +702,7 @@ hipError_t launch_reduce(const float* partial, int splits, int M, int N, Epi epi
   return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int WAVES_M, int NS, bool DUAL, int NW, class Epi>
+template <int BM, int BN, int BK, int WAVES_M, int NS, bool DUAL, int NW, int MI = 32, class Epi>
 hipError_t launch_dma(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, int N, int K, Epi epi, int splits,
                       float* partial, hipStream_t st) {
   const int bn_out = DUAL ? BN / 2 : BN;
@@ -686,10 +713,10 @@ hipError_t launch_dma(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, int
   if (K % BK != 0 || K < BK || (int64_t)(splits - 1) * kps >= K) return hipErrorInvalidValue;
   dim3 grid(tiles, 1, splits);
   if (splits > 1)
-    gemm_bf16_dma<BM, BN, BK, WAVES_M, NS, DUAL, true, Epi, NW>
+    gemm_bf16_dma<BM, BN, BK, WAVES_M, NS, DUAL, true, Epi, NW, MI>
         <<<grid, NW * 64, 0, st>>>(A, lda, w, M, N, K, kps, epi, partial);
   else
-    gemm_bf16_dma<BM, BN, BK, WAVES_M, NS, DUAL, false, Epi, NW>
+    gemm_bf16_dma<BM, BN, BK, WAVES_M, NS, DUAL, false, Epi, NW, MI>
         <<<grid, NW * 64, 0, st>>>(A, lda, w, M, N, K, kps, epi, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits <= 1) return e;
@@ -735,7 +762,7 @@ hipError_t launch_bf16(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, in
                                                                          partial, st);
   }
   if (lda % 8 == 0 && M > 64 && K % kBigBK == 0)
-    return launch_dma<256, 256, kBigBK, 2, kBigStages, DUAL, kBigWaves>(A, lda, w, M, N, K, epi, splits, partial,
+    return launch_dma<256, 256, kBigBK, 2, kBigStages, DUAL, kBigWaves, kBigMI>(A, lda, w, M, N, K, epi, splits, partial,
                                                                         st);
   hipError_t e;
   if (M <= 32) {
@@ -788,10 +815,10 @@ hipError_t gemm_residual_norm_launch(const bf16* A, int64_t lda, const bf16* w, 
   if ((int64_t)(splits - 1) * kps >= K) return hipErrorInvalidValue;
   dim3 grid(tiles, 1, splits);
   if (M <= 32)
-    gemm_bf16_dma<32, 128, kSkinnyBK, 1, kSkinnyStages, false, true, EpiResidual<bf16>, 4>
+    gemm_bf16_dma<32, 128, kSkinnyBK, 1, kSkinnyStages, false, true, EpiResidual<bf16>, 4, 32>
         <<<grid, 256, 0, st>>>(A, lda, wr, M, N, K, kps, epi, partial);
   else
-    gemm_bf16_dma<64, 128, kSkinnyBK, 2, kSkinnyStages64, false, true, EpiResidual<bf16>, 4>
+    gemm_bf16_dma<64, 128, kSkinnyBK, 2, kSkinnyStages64, false, true, EpiResidual<bf16>, 4, 32>
         <<<grid, 256, 0, st>>>(A, lda, wr, M, N, K, kps, epi, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
