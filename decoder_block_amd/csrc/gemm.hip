@@ -320,27 +320,45 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
   constexpr bool kStreamW = BM <= 64;
   constexpr int A_LOADS = kStreamW ? (BM / RPB) / NW : 0;
   static_assert(!kStreamW || (BM / RPB) % NW == 0, "activation rows must fill whole load slots");
-  auto blk_of = [&](int i) { return kStreamW ? i * NW + wave : wave * LOADS + i; };
-  // this lane's source row pointer (+ chunk offset) for each of its DMA blocks
-  const bf16* src[LOADS];
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // uniform: scalar block bases
+  auto blk_of = [&](int i) { return kStreamW ? i * NW + wave_u : wave_u * LOADS + i; };
+  // Source of each DMA block: a block is RPB consecutive rows of one operand
+  // tensor (the QKV row map switches tensors at multiples of 8 rows, checked on
+  // the host), so its base pointer is uniform and lives in scalar registers,
+  // and a lane adds a 32-bit byte offset (its row within the block's 256-row
+  // tile panel, the split's first k and its chunk); each copy adds the k-tile.
+  const char* sbase[LOADS];
+  uint32_t voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int blk = blk_of(i);
-    const int r = blk * RPB + lane / CH;
+    const int r0 = blk * RPB;                 // the block's first tile row (uniform)
+    const int r = r0 + lane / CH;
     const int c = (lane % CH) ^ swz(r);
-    const bf16* p;
-    if (r < BM) {
-      p = A + (int64_t)min(m0 + r, M - 1) * lda;
+    int64_t row;                              // this lane's row relative to the base
+    int64_t ld;
+    if (r0 < BM) {
+      sbase[i] = (const char*)(A + (int64_t)m0 * lda);
+      row = min(m0 + r, M - 1) - m0;
+      ld = lda;
     } else {
-      const int rb = r - BM;
+      const int rb0 = r0 - BM, rb = r - BM;
+      int nb, n;
+      const bf16* t;
       if (DUAL) {
-        const int n = min(n0 + (rb & (BN / 2 - 1)), N - 1);
-        p = (rb < BN / 2 ? w.w0 : w.w1) + (int64_t)n * K;
+        nb = min(n0 + (rb0 & (BN / 2 - 1)), N - 1);
+        n = min(n0 + (rb & (BN / 2 - 1)), N - 1);
+        t = (rb0 < BN / 2 ? w.w0 : w.w1) + (int64_t)nb * K;
       } else {
-        p = weight_row(w, min(n0 + rb, N - 1), K);
+        nb = min(n0 + rb0, N - 1);
+        n = min(n0 + rb, N - 1);
+        t = weight_row(w, nb, K);
       }
+      sbase[i] = (const char*)t;
+      row = n - nb;
+      ld = K;
     }
-    src[i] = p + kb + c * 8;
+    voff[i] = (uint32_t)((row * ld + kb + c * 8) * 2);
   }
   // DMA of k-tile kt into ring slot kt % NS (kt is clamped to the last tile so the
   // refill at the end of the loop stays branch-free; those copies are never read)
@@ -348,15 +366,17 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
     const int st = kt % NS;
     int kc = min(kt, nk - 1) + krot;
     kc = kc >= nk ? kc - nk : kc;
+    const uint32_t kbyte = (uint32_t)(kc * BK * 2);
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
       LLAMA_LDS void* dst = (LLAMA_LDS void*)&smem[st][blk_of(i) * 64];
-      __builtin_amdgcn_global_load_lds((const void*)(src[i] + kc * BK), dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(sbase[i] + (voff[i] + kbyte)), dst, 16, 0, 0);
     }
 #pragma unroll
     for (int i = A_LOADS; i < LOADS; ++i) {
       LLAMA_LDS void* dst = (LLAMA_LDS void*)&smem[st][blk_of(i) * 64];
-      __builtin_amdgcn_global_load_lds((const void*)(src[i] + kc * BK), dst, 16, 0, kStreamW ? kCpolNT : 0);
+      __builtin_amdgcn_global_load_lds((const void*)(sbase[i] + (voff[i] + kbyte)), dst, 16, 0,
+                                       kStreamW ? kCpolNT : 0);
     }
   };
   auto wrow = [&](int t) {
@@ -448,60 +468,67 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
   // no DMA may still be writing LDS when the workgroup retires
   wait_vmcnt<0>();
 
-  // accumulator element g*4 + i of acc[a][b] is output row m = (b * MI + lrow)
-  // and column n = a * MI + g * 8 + lk * 4 + i of the wave's tile
+  // Accumulator element g*4 + i of acc[a][b] is output row m = (b * MI + lrow)
+  // and column n = a * MI + g * 8 + lk * 4 + i of the wave's tile.  The lane's
+  // coordinates are recomputed here instead of being kept live through the
+  // k-loop, which needs every VGPR (kept, a few of them spilled to scratch).
+  {
+    const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int lrow = lane % MI, lk = lane / MI;
+    const int wm = wave_u % WAVES_M, wn = wave_u / WAVES_M;
 #pragma unroll
-  for (int b = 0; b < TM; ++b) {
-    const int m = m0 + wm * WM + b * MI + lrow;
-    if (m >= M) continue;
-    if constexpr (DUAL) {
+    for (int b = 0; b < TM; ++b) {
+      const int m = m0 + wm * WM + b * MI + lrow;
+      if (m >= M) continue;
+      if constexpr (DUAL) {
 #pragma unroll
-      for (int a = 0; a < TN / 2; ++a)
+        for (int a = 0; a < TN / 2; ++a)
 #pragma unroll
-        for (int g = 0; g < NV; ++g) {
-          const int n = n0 + wn * (WN / 2) + a * MI + g * 8 + lk * 4;
-          if (n >= N) continue;
-          f32x4 v1 = {acc[a][b][g * 4], acc[a][b][g * 4 + 1], acc[a][b][g * 4 + 2], acc[a][b][g * 4 + 3]};
-          const acc_t& a3 = acc[a + TN / 2][b];
-          f32x4 v3 = {a3[g * 4], a3[g * 4 + 1], a3[g * 4 + 2], a3[g * 4 + 3]};
-          if (SPLIT) {
-            float* p = partial + ((int64_t)blockIdx.z * M + m) * (2 * (int64_t)N);
-            *(f32x4*)(p + n) = v1;
-            *(f32x4*)(p + N + n) = v3;
-          } else {
-            epi(m, n, v1, v3);
+          for (int g = 0; g < NV; ++g) {
+            const int n = n0 + wn * (WN / 2) + a * MI + g * 8 + lk * 4;
+            if (n >= N) continue;
+            f32x4 v1 = {acc[a][b][g * 4], acc[a][b][g * 4 + 1], acc[a][b][g * 4 + 2], acc[a][b][g * 4 + 3]};
+            const acc_t& a3 = acc[a + TN / 2][b];
+            f32x4 v3 = {a3[g * 4], a3[g * 4 + 1], a3[g * 4 + 2], a3[g * 4 + 3]};
+            if (SPLIT) {
+              float* p = partial + ((int64_t)blockIdx.z * M + m) * (2 * (int64_t)N);
+              *(f32x4*)(p + n) = v1;
+              *(f32x4*)(p + N + n) = v3;
+            } else {
+              epi(m, n, v1, v3);
+            }
           }
-        }
-    } else if constexpr (SPLIT) {
+      } else if constexpr (SPLIT) {
 #pragma unroll
-      for (int a = 0; a < TN; ++a)
+        for (int a = 0; a < TN; ++a)
 #pragma unroll
-        for (int g = 0; g < NV; ++g) {
-          const int n = n0 + wn * WN + a * MI + g * 8 + lk * 4;
-          if (n >= N) continue;
-          f32x4 v = {acc[a][b][g * 4], acc[a][b][g * 4 + 1], acc[a][b][g * 4 + 2], acc[a][b][g * 4 + 3]};
-          *(f32x4*)(partial + ((int64_t)blockIdx.z * M + m) * (int64_t)N + n) = v;
-        }
-    } else {
-      // row-dependent parts once, then the fragment's epilogue loads, then its stores
-      const auto row = epi_row(epi, m);
-      decltype(epi_pre(epi, row, 0)) pre[TN][NV];
+          for (int g = 0; g < NV; ++g) {
+            const int n = n0 + wn * WN + a * MI + g * 8 + lk * 4;
+            if (n >= N) continue;
+            f32x4 v = {acc[a][b][g * 4], acc[a][b][g * 4 + 1], acc[a][b][g * 4 + 2], acc[a][b][g * 4 + 3]};
+            *(f32x4*)(partial + ((int64_t)blockIdx.z * M + m) * (int64_t)N + n) = v;
+          }
+      } else {
+        // row-dependent parts once, then the fragment's epilogue loads, then its stores
+        const auto row = epi_row(epi, m);
+        decltype(epi_pre(epi, row, 0)) pre[TN][NV];
 #pragma unroll
-      for (int a = 0; a < TN; ++a)
+        for (int a = 0; a < TN; ++a)
 #pragma unroll
-        for (int g = 0; g < NV; ++g) {
-          const int n = n0 + wn * WN + a * MI + g * 8 + lk * 4;
-          pre[a][g] = epi_pre(epi, row, min(n, N - 4));
-        }
+          for (int g = 0; g < NV; ++g) {
+            const int n = n0 + wn * WN + a * MI + g * 8 + lk * 4;
+            pre[a][g] = epi_pre(epi, row, min(n, N - 4));
+          }
 #pragma unroll
-      for (int a = 0; a < TN; ++a)
+        for (int a = 0; a < TN; ++a)
 #pragma unroll
-        for (int g = 0; g < NV; ++g) {
-          const int n = n0 + wn * WN + a * MI + g * 8 + lk * 4;
-          if (n >= N) continue;
-          f32x4 v = {acc[a][b][g * 4], acc[a][b][g * 4 + 1], acc[a][b][g * 4 + 2], acc[a][b][g * 4 + 3]};
-          epi_apply(epi, row, n, v, pre[a][g]);
-        }
+          for (int g = 0; g < NV; ++g) {
+            const int n = n0 + wn * WN + a * MI + g * 8 + lk * 4;
+            if (n >= N) continue;
+            f32x4 v = {acc[a][b][g * 4], acc[a][b][g * 4 + 1], acc[a][b][g * 4 + 2], acc[a][b][g * 4 + 3]};
+            epi_apply(epi, row, n, v, pre[a][g]);
+          }
+      }
     }
   }
 }
@@ -744,8 +771,12 @@ template <bool DUAL, class Epi>
 hipError_t launch_bf16(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, int N, int K, Epi epi,
                        int splits, float* partial, hipStream_t st) {
   // the DMA-pipelined kernels need K (and each split's K range) in whole k-tiles
-  // (BK = kSkinnyBK for small M, kBigBK otherwise) and 16-byte aligned rows
-  if (lda % 8 == 0 && M <= 64 && K % kSkinnyBK == 0) {
+  // (BK = kSkinnyBK for small M, kBigBK otherwise), 16-byte aligned rows, the
+  // row map's tensor boundaries on multiples of 8 rows (one tensor per DMA
+  // block) and 32-bit byte offsets within a 256-row panel
+  const bool dma_ok = lda % 8 == 0 && w.n1 % 8 == 0 && w.n2 % 8 == 0 &&
+                      (int64_t)256 * (lda > K ? lda : K) * 2 < ((int64_t)1 << 32);
+  if (dma_ok && M <= 64 && K % kSkinnyBK == 0) {
     if (M <= 32) {
       if constexpr (DUAL)
         return launch_dma<32, 256, kSkinnyBK, 1, kSkinnyStages, DUAL, 4>(A, lda, w, M, N, K, epi, splits,
@@ -761,7 +792,7 @@ hipError_t launch_bf16(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, in
       return launch_dma<64, 128, kSkinnyBK, 2, kSkinnyStages64, DUAL, 4>(A, lda, w, M, N, K, epi, splits,
                                                                          partial, st);
   }
-  if (lda % 8 == 0 && M > 64 && K % kBigBK == 0)
+  if (dma_ok && M > 64 && K % kBigBK == 0)
     return launch_dma<256, 256, kBigBK, 2, kBigStages, DUAL, kBigWaves, kBigMI>(A, lda, w, M, N, K, epi, splits, partial,
                                                                         st);
   hipError_t e;
@@ -799,6 +830,7 @@ hipError_t launch_f32(const float* A, int64_t lda, WeightRows<float> w, int M, i
 
 bool gemm_residual_norm_fits(int M, int N, int K, int64_t lda) {
   return M > kGemvMaxM && M <= 64 && N % 4 == 0 && lda % 8 == 0 && K % kSkinnyBK == 0 &&
+         (int64_t)256 * (lda > K ? lda : K) * 2 < ((int64_t)1 << 32) &&
          gemm_pick_splits(M, N, K, false, true) > 1;
 }
 
