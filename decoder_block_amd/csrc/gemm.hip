@@ -476,8 +476,60 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
     const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     const int lrow = lane % MI, lk = lane / MI;
     const int wm = wave_u % WAVES_M, wn = wave_u / WAVES_M;
+    using pre_t = decltype(epi_pre(epi, epi_row(epi, 0), 0));
+    using row_t = decltype(epi_row(epi, 0));
+    // Epilogues with pre-loads (the residual, the RoPE table) fetch them for a
+    // batch of the wave's rows before any of those rows' stores: the stores may
+    // alias the loads (in-place residual), so the compiler would otherwise wait
+    // out one load round trip per store (residual).  A quarter of the rows per
+    // batch for 8-byte pre-loads, one row for the 16-byte (cos, sin) pairs:
+    // more next to the accumulators spill VGPRs.  Rows past M and columns past
+    // N load a clamped, valid element.
+    constexpr bool kBatched = !DUAL && !SPLIT && !std::is_same<pre_t, NoPre>::value;
+    if constexpr (kBatched) {
+      constexpr int HB = (sizeof(pre_t) <= 8 && TM > 2) ? TM / 4 : 1;
+#pragma unroll
+      for (int b0 = 0; b0 < TM; b0 += HB) {
+        pre_t pre[HB][TN][NV];
+        row_t rows[HB];
+#pragma unroll
+        for (int bb = 0; bb < HB; ++bb) {
+          const int m = min(m0 + wm * WM + (b0 + bb) * MI + lrow, M - 1);
+          rows[bb] = epi_row(epi, m);
+#pragma unroll
+          for (int a = 0; a < TN; ++a)
+#pragma unroll
+            for (int g = 0; g < NV; ++g) {
+              const int n = n0 + wn * WN + a * MI + g * 8 + lk * 4;
+              pre[bb][a][g] = epi_pre(epi, rows[bb], min(n, N - 4));
+            }
+        }
+#pragma unroll
+        for (int bb = 0; bb < HB; ++bb) {
+          const int b = b0 + bb;
+          const int m = m0 + wm * WM + b * MI + lrow;
+          if (m >= M) continue;
+#pragma unroll
+          for (int a = 0; a < TN; ++a)
+#pragma unroll
+            for (int g = 0; g < NV; ++g) {
+              const int n = n0 + wn * WN + a * MI + g * 8 + lk * 4;
+              if (n >= N) continue;
+              f32x4 v = {acc[a][b][g * 4], acc[a][b][g * 4 + 1], acc[a][b][g * 4 + 2], acc[a][b][g * 4 + 3]};
+              epi_apply(epi, rows[bb], n, v, pre[bb][a][g]);
+            }
+        }
+      }
+    }
+    // the dual epilogue's per-row factors, all fetched before the first store
+    float rsc[DUAL && !SPLIT ? TM : 1];
+    if constexpr (DUAL && !SPLIT) {
+#pragma unroll
+      for (int b = 0; b < TM; ++b) rsc[b] = epi.row_scale(min(m0 + wm * WM + b * MI + lrow, M - 1));
+    }
 #pragma unroll
     for (int b = 0; b < TM; ++b) {
+      if constexpr (kBatched) break;
       const int m = m0 + wm * WM + b * MI + lrow;
       if (m >= M) continue;
       if constexpr (DUAL) {
@@ -490,12 +542,12 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
             f32x4 v1 = {acc[a][b][g * 4], acc[a][b][g * 4 + 1], acc[a][b][g * 4 + 2], acc[a][b][g * 4 + 3]};
             const acc_t& a3 = acc[a + TN / 2][b];
             f32x4 v3 = {a3[g * 4], a3[g * 4 + 1], a3[g * 4 + 2], a3[g * 4 + 3]};
-            if (SPLIT) {
+            if constexpr (SPLIT) {
               float* p = partial + ((int64_t)blockIdx.z * M + m) * (2 * (int64_t)N);
               *(f32x4*)(p + n) = v1;
               *(f32x4*)(p + N + n) = v3;
             } else {
-              epi(m, n, v1, v3);
+              epi.apply(m, n, v1, v3, rsc[b]);
             }
           }
       } else if constexpr (SPLIT) {

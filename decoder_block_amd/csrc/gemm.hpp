@@ -115,6 +115,17 @@ __device__ __forceinline__ void epi_apply(const Epi& e, int m, int n, f32x4 v, N
   e(m, n, v);
 }
 
+// The residual epilogue's pre-load is the residual group itself (8 bytes in
+// bf16), small enough that the GEMM kernel fetches a wave's whole tile of them
+// before its first store.
+__device__ __forceinline__ bf16x4 epi_pre(const EpiResidual<bf16>& e, int m, int n) {
+  return *(const bf16x4*)(e.r + (int64_t)m * e.ld + n);
+}
+__device__ __forceinline__ void epi_apply(const EpiResidual<bf16>& e, int m, int n, f32x4 v, bf16x4 r) {
+  const f32x4 rv = {(float)r[0], (float)r[1], (float)r[2], (float)r[3]};
+  store4(e.y + (int64_t)m * e.ld + n, rv + v);
+}
+
 template <typename T>
 struct QkvRow {
   T* q;              // q_out row
@@ -151,16 +162,19 @@ struct EpiSwiGLU {
   T* g;
   int64_t ldg;
   const float* rscale; // optional per-row RMSNorm factor applied to both accumulators
-  __device__ __forceinline__ void operator()(int m, int n, f32x4 a1, f32x4 a3) const {
-    if (rscale) {
-      const float r = rscale[m];
-      a1 *= r;
-      a3 *= r;
-    }
+  __device__ __forceinline__ float row_scale(int m) const { return rscale ? rscale[m] : 1.0f; }
+  // with the row factor r fetched beforehand (the GEMM kernel loads a wave's
+  // factors before its first store, which they could otherwise not pass)
+  __device__ __forceinline__ void apply(int m, int n, f32x4 a1, f32x4 a3, float r) const {
+    a1 *= r;
+    a3 *= r;
     f32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = a1[i] / (1.0f + __expf(-a1[i])) * a3[i];
     store4(g + (int64_t)m * ldg + n, o);
+  }
+  __device__ __forceinline__ void operator()(int m, int n, f32x4 a1, f32x4 a3) const {
+    apply(m, n, a1, a3, row_scale(m));
   }
 };
 
