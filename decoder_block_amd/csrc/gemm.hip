@@ -425,6 +425,9 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
   };
 
   constexpr int KS = BK / KM;                 // MFMA steps per k-tile
+  // (the fragment double buffer alternates per step and restarts at buffer 0
+  // on every k-tile, which takes an even step count)
+  static_assert(KS % 2 == 0, "MFMA steps per k-tile");
   bf16x8 fa[2][TN], fb[2][TM];
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) issue(s);
@@ -826,7 +829,8 @@ hipError_t launch_bf16(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, in
   // (BK = kSkinnyBK for small M, kBigBK otherwise), 16-byte aligned rows, the
   // row map's tensor boundaries on multiples of 8 rows (one tensor per DMA
   // block) and 32-bit byte offsets within a 256-row panel
-  const bool dma_ok = lda % 8 == 0 && w.n1 % 8 == 0 && w.n2 % 8 == 0 &&
+  const bool one_tensor = w.n1 >= N && w.n2 >= N;
+  const bool dma_ok = lda % 8 == 0 && (one_tensor || (w.n1 % 8 == 0 && w.n2 % 8 == 0)) &&
                       (int64_t)256 * (lda > K ? lda : K) * 2 < ((int64_t)1 << 32);
   if (dma_ok && M <= 64 && K % kSkinnyBK == 0) {
     if (M <= 32) {
