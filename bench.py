@@ -165,6 +165,15 @@ def time_decode(r, xs, p0s, flush):
     return tot, [s / n for s in stage_tot]
 
 
+def sources_hash(paths):
+    """sha256 (16 hex digits) over the kernel's source files, in the given order."""
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def kernel_traffic(kernel_key):
     """HBM traffic per launch from the committed rocprofv3 PMC summary, or None when the
     kernel source changed since the counters were taken."""
@@ -175,9 +184,7 @@ def kernel_traffic(kernel_key):
         with open(p) as f:
             d = json.load(f)
         ent = d[kernel_key]
-        src = os.path.join(ROOT, ent["source"])
-        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-        return ent["bytes_per_launch"] if h == ent["source_sha256_16"] else None
+        return ent["bytes_per_launch"] if sources_hash(ent["sources"]) == ent["sources_sha256_16"] else None
     except Exception:
         return None
 
