@@ -35,6 +35,10 @@ constexpr int kBigWaves = 8;
 // faster, at the same LDS traffic and the same number of waves.
 constexpr int kBigMI = 16;
 constexpr int kCUs = 256;         // MI355X compute units
+// Unsplit 256 x 256 tiles run on a resident grid that walks the tiles (measured
+// at M = 131072: 1-2 % faster for K = 2048-8192, 0.3-0.5 % at K = 14336 or
+// N = 14336; the same at M = 8192)
+constexpr bool kResidentLargeTiles = true;
 // small M (<= 64 tokens: the weights stream from HBM once): 64-deep k-tiles
 // (128-byte row pieces).  Tiles: M <= 32: 32 rows x 128 columns, 32 x 256 for
 // the dual w1/w3 kernel; 33..64 rows: 64 x 128.  Narrow tiles need fewer
@@ -59,10 +63,10 @@ __device__ __forceinline__ const T* weight_row(const WeightRows<T>& w, int n, in
 
 // Tile coordinates of a logical workgroup id: XCD-aware remap, then grouped
 // ordering (GROUP_M tile rows share their weight tiles in L2).
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn, int bid) {
   constexpr int GROUP_M = 4;
   int nb = tiles_m * tiles_n;
-  int pid = xcd_remap(blockIdx.x, nb);
+  int pid = xcd_remap(bid, nb);
   int in_group = GROUP_M * tiles_n;
   int gid = pid / in_group;
   int first_m = gid * GROUP_M;
@@ -98,7 +102,7 @@ gemm_bf16_mfma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int 
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (N + BN_OUT - 1) / BN_OUT;
   int tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
+  tile_coords(tiles_m, tiles_n, tm, tn, (int)blockIdx.x);
   const int m0 = tm * BM, n0 = tn * BN_OUT;
   const int kb = blockIdx.z * k_per_split;
   const int ke = min(K, kb + k_per_split);
@@ -295,12 +299,25 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
   static_assert(WAVES_M * WAVES_N == NW, "waves");
   __shared__ bf16x8 smem[NS][ROWS * CH];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+  const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar block bases
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (N + BN_OUT - 1) / BN_OUT;
+  // Unsplit large tiles run on a resident grid (as many workgroups as the CUs
+  // hold at once), each walking the tiles with a stride of the grid size, in
+  // the logical order one workgroup per tile would take: every XCD keeps its
+  // range of tiles, and no workgroup launch or set-up separates two tiles.
+  constexpr bool kResident = kResidentLargeTiles && BM > 64 && !SPLIT;
+  auto tile = [&](int vt) __attribute__((always_inline)) {
+  // On the resident grid the thread's coordinates are derived per tile from the
+  // thread id and an opaque zero: the compiler then cannot hoist them out of
+  // the tile loop and keep them live through the epilogue, where the
+  // accumulators need every VGPR.
+  uint32_t zero = 0;
+  if constexpr (kResident) asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+  const int tid = (int)(threadIdx.x ^ zero), lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
   int tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
+  tile_coords(tiles_m, tiles_n, tm, tn, vt);
   const int m0 = tm * BM, n0 = tn * BN_OUT;
   const int kb = blockIdx.z * k_per_split;
   const int nk = (min(K, kb + k_per_split) - kb) / BK;
@@ -320,7 +337,6 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
   constexpr bool kStreamW = BM <= 64;
   constexpr int A_LOADS = kStreamW ? (BM / RPB) / NW : 0;
   static_assert(!kStreamW || (BM / RPB) % NW == 0, "activation rows must fill whole load slots");
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // uniform: scalar block bases
   auto blk_of = [&](int i) { return kStreamW ? i * NW + wave_u : wave_u * LOADS + i; };
   // Source of each DMA block: a block is RPB consecutive rows of one operand
   // tensor (the QKV row map switches tensors at multiples of 8 rows, checked on
@@ -586,6 +602,17 @@ gemm_bf16_dma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int M
       }
     }
   }
+  };
+  if constexpr (kResident) {
+    const int ntile = tiles_m * tiles_n;
+    for (int vt = blockIdx.x; vt < ntile; vt += (int)gridDim.x) {
+      // every wave is past the previous tile's reads of the ring
+      if (vt != (int)blockIdx.x) __builtin_amdgcn_s_barrier();
+      tile(vt);
+    }
+  } else {
+    tile((int)blockIdx.x);
+  }
 }
 
 // ------------------------------------------------------------------ fp32 FMA kernel
@@ -601,7 +628,7 @@ gemm_f32_fma(const float* __restrict__ A, int64_t lda, WeightRows<float> w, int 
   const int tid = threadIdx.x;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
+  tile_coords(tiles_m, tiles_n, tm, tn, (int)blockIdx.x);
   const int m0 = tm * BM, n0 = tn * BN;
   const int kb = blockIdx.z * k_per_split, ke = min(K, kb + k_per_split);
   const int tx = tid % 16, ty = tid / 16;  // n block tx*4, m block ty*4
@@ -784,6 +811,21 @@ hipError_t launch_reduce(const float* partial, int splits, int M, int N, Epi epi
   return hipGetLastError();
 }
 
+// Workgroups of `kernel` resident at once on the current device (CUs x blocks per
+// CU), or 0 if the runtime cannot say.  The CU count is read once per process.
+int resident_blocks(const void* kernel, int threads) {
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    return n;
+  }();
+  int per = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess) return 0;
+  return cus * per;
+}
+
 template <int BM, int BN, int BK, int WAVES_M, int NS, bool DUAL, int NW, int MI = 32, class Epi>
 hipError_t launch_dma(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, int N, int K, Epi epi, int splits,
                       float* partial, hipStream_t st) {
@@ -794,12 +836,18 @@ hipError_t launch_dma(const bf16* A, int64_t lda, WeightRows<bf16> w, int M, int
   // every split must own at least one whole k-tile
   if (K % BK != 0 || K < BK || (int64_t)(splits - 1) * kps >= K) return hipErrorInvalidValue;
   dim3 grid(tiles, 1, splits);
-  if (splits > 1)
+  if (splits > 1) {
     gemm_bf16_dma<BM, BN, BK, WAVES_M, NS, DUAL, true, Epi, NW, MI>
         <<<grid, NW * 64, 0, st>>>(A, lda, w, M, N, K, kps, epi, partial);
-  else
-    gemm_bf16_dma<BM, BN, BK, WAVES_M, NS, DUAL, false, Epi, NW, MI>
-        <<<grid, NW * 64, 0, st>>>(A, lda, w, M, N, K, kps, epi, partial);
+  } else {
+    auto* kern = gemm_bf16_dma<BM, BN, BK, WAVES_M, NS, DUAL, false, Epi, NW, MI>;
+    if (kResidentLargeTiles && BM > 64) {
+      const int res = resident_blocks((const void*)kern, NW * 64);
+      if (res <= 0) return hipErrorInvalidDeviceFunction;
+      grid.x = (unsigned)std::min(tiles, res);
+    }
+    kern<<<grid, NW * 64, 0, st>>>(A, lda, w, M, N, K, kps, epi, partial);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits <= 1) return e;
   return launch_reduce<DUAL, Epi>(partial, splits, M, N, epi, st);
