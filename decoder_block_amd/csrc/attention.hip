@@ -312,43 +312,52 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
           if (t > qpos) sacc[kt][v] = -INFINITY;
         }
     }
-    float mraw = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mraw = fmaxf(mraw, sacc[kt][v]);
-    mraw = pair_max32(mraw);
-    const float mt = mraw * scale_log2;       // tile max in the log2 domain (scale > 0)
-    // lazy rescale: the running max moves only when some row's max grows by more
-    // than 8 (probabilities then stay below 2^8); the result is unchanged
-    if (__any(mt > m_run + 8.0f)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < HD / 32; ++dt) oacc[dt] *= alpha;
-      m_run = m_new;
-    }
+    // Probabilities against the running max (log2 domain, scale > 0) and their
+    // row sum exactly as P.V uses them (bf16, two per dot2).
     bf16x8 pf[2][2];
+    float psum;
+    auto probs = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        pf[kt][v >> 3][v & 7] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][v], scale_log2, -m_run));
-    // the row sum of the probabilities exactly as P.V uses them (bf16), two per dot2
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
-    const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
+        for (int v = 0; v < 16; ++v)
+          pf[kt][v >> 3][v & 7] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][v], scale_log2, -m_run));
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+      const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
+        for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bf16x2 pp = {pf[kt][h2][2 * j], pf[kt][h2][2 * j + 1]};
-          ps[j] = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, ps[j], false);
-        }
-    float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    psum = pair_sum32(psum);
+          for (int j = 0; j < 4; ++j) {
+            const bf16x2 pp = {pf[kt][h2][2 * j], pf[kt][h2][2 * j + 1]};
+            ps[j] = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, ps[j], false);
+          }
+      psum = pair_sum32((ps[0] + ps[1]) + (ps[2] + ps[3]));
+    };
+    probs();
+    // Lazy rescale: the running max moves only when some row's max grows by more
+    // than 8 (probabilities then stay below 2^8).  A row sum of at most 2^8 bounds
+    // every probability of the row, so the tile max is only taken when some row's
+    // sum exceeds it (or is not finite: the first tile, against a max of -inf).
+    if (__any(!(psum <= 256.0f))) {
+      float mraw = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mraw = fmaxf(mraw, sacc[kt][v]);
+      mraw = pair_max32(mraw);
+      const float mt = mraw * scale_log2;
+      if (__any(mt > m_run + 8.0f)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < HD / 32; ++dt) oacc[dt] *= alpha;
+        m_run = m_new;
+        probs();
+      }
+    }
     l_run += psum;
 
 #pragma unroll
