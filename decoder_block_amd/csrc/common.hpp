@@ -35,6 +35,12 @@ __device__ __forceinline__ void store4(bf16* p, f32x4 v) {
   bf16x4 o = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
   *(bf16x4*)p = o;
 }
+// 8 consecutive values (lo, hi) as one 16-byte store; p 16-byte aligned
+__device__ __forceinline__ void store8(bf16* p, f32x4 lo, f32x4 hi) {
+  bf16x8 o = {(bf16)lo[0], (bf16)lo[1], (bf16)lo[2], (bf16)lo[3], (bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
+  *(bf16x8*)p = o;
+}
+__device__ __forceinline__ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 // 16-byte load with the non-temporal hint, for data read exactly once (weights
 // streamed by the one-token projections, the KV rows of a decode step): it does
@@ -61,6 +67,19 @@ __device__ __forceinline__ float wave_max(float v) {
 // instructions instead of an LDS permute.  A swap of v with itself leaves, in
 // its two results, v[l] and v[l ^ off] (in an order that depends on the lane),
 // and both ops are symmetric, so every lane of a pair gets the same value.
+// Lane rows (16 lanes each) 0/1 and 2/3 trade halves of two 4-vectors: a lane
+// of row r gets, as lo and hi, the values of rows r & ~1 and r | 1 of x (r even)
+// or of y (r odd).  With x, y holding 4 consecutive columns per lane row of two
+// 16-column tiles (row r: columns 4r..4r+3), lo/hi become 8 consecutive columns:
+// row 0 tile x columns 0-7, row 1 tile y 0-7, row 2 tile x 8-15, row 3 tile y 8-15.
+__device__ __forceinline__ void pair_transpose16(const f32x4& x, const f32x4& y, f32x4& lo, f32x4& hi) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[v]), __float_as_uint(y[v]), false, false);
+    lo[v] = __uint_as_float(r[0]);
+    hi[v] = __uint_as_float(r[1]);
+  }
+}
 __device__ __forceinline__ float pair_max16(float v) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));

@@ -181,7 +181,90 @@ struct EpiSwiGLU {
   __device__ __forceinline__ void operator()(int m, int n, f32x4 a1, f32x4 a3) const {
     apply(m, n, a1, a3, row_scale(m));
   }
+  __device__ __forceinline__ static f32x4 silu_mul(f32x4 a1, f32x4 a3) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    f32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = a1[i] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a1[i] * kLog2e)) * a3[i];
+    return o;
+  }
+  // columns n..n+7 (lo, hi of both products) as one 16-byte store
+  __device__ __forceinline__ void apply8(int m, int n, f32x4 a1lo, f32x4 a1hi, f32x4 a3lo, f32x4 a3hi,
+                                         float r) const {
+    store8(g + (int64_t)m * ldg + n, silu_mul(a1lo * r, a3lo * r), silu_mul(a1hi * r, a3hi * r));
+  }
 };
+
+// 8-column forms, used by the large-tile kernel on interior tiles when every
+// row it writes (and reads) is 16-byte aligned: columns n..n+7 (n a multiple
+// of 8) arrive as lo = n..n+3 and hi = n+4..n+7 and are stored as 16 bytes.
+// epi_vec8_ok says whether an epilogue's pointers and row strides allow it.
+template <class Epi>
+__device__ __forceinline__ bool epi_vec8_ok(const Epi&) {
+  return false;
+}
+template <class Epi, class Row>
+__device__ __forceinline__ NoPre epi_pre8(const Epi&, const Row&, int) {
+  return {};
+}
+
+__device__ __forceinline__ bool epi_vec8_ok(const EpiStore<bf16>& e) { return e.ldy % 8 == 0 && aligned16(e.y); }
+__device__ __forceinline__ void epi_apply8(const EpiStore<bf16>& e, int m, int n, f32x4 lo, f32x4 hi, NoPre) {
+  store8(e.y + (int64_t)m * e.ldy + n, lo, hi);
+}
+
+__device__ __forceinline__ bool epi_vec8_ok(const EpiF32& e) { return e.ldy % 4 == 0 && aligned16(e.y); }
+__device__ __forceinline__ void epi_apply8(const EpiF32& e, int m, int n, f32x4 lo, f32x4 hi, NoPre) {
+  float* p = e.y + (int64_t)m * e.ldy + n;
+  store4(p, lo);
+  store4(p + 4, hi);
+}
+
+__device__ __forceinline__ bool epi_vec8_ok(const EpiResidual<bf16>& e) {
+  return e.ld % 8 == 0 && aligned16(e.y) && aligned16(e.r);
+}
+__device__ __forceinline__ bf16x8 epi_pre8(const EpiResidual<bf16>& e, int m, int n) {
+  return *(const bf16x8*)(e.r + (int64_t)m * e.ld + n);
+}
+__device__ __forceinline__ void epi_apply8(const EpiResidual<bf16>& e, int m, int n, f32x4 lo, f32x4 hi, bf16x8 r) {
+  const f32x4 rlo = {(float)r[0], (float)r[1], (float)r[2], (float)r[3]};
+  const f32x4 rhi = {(float)r[4], (float)r[5], (float)r[6], (float)r[7]};
+  store8(e.y + (int64_t)m * e.ld + n, rlo + lo, rhi + hi);
+}
+
+// (cos, sin) of the four column pairs of columns n..n+7
+struct CosSin8 {
+  f32x4 lo, hi;
+};
+template <typename T>
+__device__ __forceinline__ bool epi_vec8_ok(const EpiQKV<T>& e) {
+  return sizeof(T) == 2 && e.nq % 8 == 0 && e.nkv % 8 == 0 && e.head_dim % 8 == 0 && aligned16(e.q_out) &&
+         aligned16(e.cache_k) && aligned16(e.cache_v) && aligned16(e.freqs);
+}
+template <typename T>
+__device__ __forceinline__ CosSin8 epi_pre8(const EpiQKV<T>& e, const QkvRow<T>& r, int n) {
+  const int c = n < e.nq ? n : n - e.nq;   // v columns load a harmless table entry
+  const float* t = r.cs + (c & (e.head_dim - 1));
+  return CosSin8{*(const f32x4*)t, *(const f32x4*)(t + 4)};
+}
+template <typename T>
+__device__ __forceinline__ void epi_apply8(const EpiQKV<T>& e, const QkvRow<T>& r, int n, f32x4 lo, f32x4 hi,
+                                           CosSin8 cs) {
+  lo *= r.scale;
+  hi *= r.scale;
+  const bool is_q = n < e.nq, is_v = n >= e.nq + e.nkv;
+  const f32x4 olo = is_v ? lo : EpiQKV<T>::rotate(lo, cs.lo);
+  const f32x4 ohi = is_v ? hi : EpiQKV<T>::rotate(hi, cs.hi);
+  T* dst = is_q ? r.q + n : (is_v ? r.v + (n - e.nq - e.nkv) : r.k + (n - e.nq));
+  store8(dst, olo, ohi);
+}
+
+// the dual epilogue over 8 columns, with the row factor fetched beforehand
+template <typename T>
+__device__ __forceinline__ bool epi_vec8_ok(const EpiSwiGLU<T>& e) {
+  return sizeof(T) == 2 && e.ldg % 8 == 0 && aligned16(e.g);
+}
 
 // Host-side launch helpers (gemm.hip).  `splits` > 1 runs split-K: partial
 // sums go to `partial` (fp32, splits * M * N_out * (dual ? 2 : 1) floats) and a
