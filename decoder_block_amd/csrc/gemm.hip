@@ -248,20 +248,22 @@ gemm_bf16_mfma(const bf16* __restrict__ A, int64_t lda, WeightRows<bf16> w, int 
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel, LDS DMA pipeline
-// Large-M variant: 256 x 256 output tile, BK = 32, NS-stage ring of LDS tiles
-// filled by global_load_lds_dwordx4 (global memory straight into LDS, no
-// staging registers), so NS-1 k-tiles are in flight while one is consumed.
-// Each DMA instruction writes 1 KiB = 16 tile rows x 64 B; lane l of block b
-// fetches row b*16 + l/4, 16-byte chunk (l%4) ^ ((l/16)%4): the XOR swizzle
-// makes the 16 lanes of each ds_read_b128 phase (16 consecutive rows, one
-// chunk) hit 16 distinct 16-byte bank groups.  Rows past M or N read a
-// clamped (valid) row whose products land only in discarded outputs; K must
-// be a multiple of 32.
-// Schedule per k-tile: the fragments of each 16-deep half are read from LDS
-// while the previous half's 16 MFMAs run, the next tile's first half is read
-// right after the single s_barrier, and the DMA refill of the ring slot just
-// consumed is issued after that barrier.  The vmcnt waits are explicit: the
-// compiler cannot see the LDS writes of the DMA.
+// BM x BN output tile (256 x 256 for large M; 32 or 64 rows for decode-sized
+// M), BK-deep k-tiles (32 or 64) in an NS-stage ring of LDS tiles filled by
+// global_load_lds_dwordx4 (global memory straight into LDS, no staging
+// registers), so NS-1 k-tiles are in flight while one is consumed.  Each DMA
+// instruction writes 1 KiB = 64 lanes x 16 bytes, RPB = 1024 / (2 BK) tile rows:
+// lane l fetches row l / CH of its block (CH = BK / 8 chunks per row), 16-byte
+// chunk (l % CH) ^ swz(row).  The XOR swizzle makes the 16 lanes of each
+// ds_read_b128 phase (16 consecutive rows, one chunk) hit 16 distinct 16-byte
+// bank groups.  Rows past M or N read a clamped (valid) row whose products land
+// only in discarded outputs; K must be a multiple of BK.
+// Schedule per k-tile: KS = BK / KM MFMA steps (KM = 16 or 32 deep).  The
+// fragments of each step are read from LDS while the previous step's MFMAs run,
+// the next k-tile's first fragments are read right after the single s_barrier,
+// and the DMA refill of the ring slot just consumed is issued after that
+// barrier.  The vmcnt waits are explicit: the compiler cannot see the LDS
+// writes of the DMA.
 #define LLAMA_LDS __attribute__((address_space(3)))
 
 template <int N>
