@@ -190,6 +190,7 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
   const int s_c = row_valid ? s : S - 1;
   const int qpos = p0 + s;
   const int wave_qmin = p0 + qb * BQ + (wave * 32) % BQ;   // smallest query position of this wave
+  const int wave_qmax = wave_qmin + min(32, BQ) - 1;        // and its largest
 
   bf16x8 qf[HD / 16];
   {
@@ -276,6 +277,8 @@ attn_prefill_mfma(const bf16* __restrict__ q, const bf16* __restrict__ ck, const
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (it + 1 < ntiles) issue(t0 + BKV, std::integral_constant<int, ST ^ 1>{});
+    // a tile above all of this wave's rows is fully masked for it: nothing to add
+    if (t0 > wave_qmax) return;
 
     // S^T = K.Q^T: the K fragment reads run AHEAD reads in front of the MFMAs
     // that consume them (left to itself the compiler kept one or two reads in

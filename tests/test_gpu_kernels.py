@@ -92,6 +92,10 @@ def test_rope_apply(dtype):
     ("bf16", 200, 1000, 260),     # large tiles, K not a multiple of 32 (register-staged kernel)
     ("bf16", 257, 64, 256),       # a single k-tile pair, one row past a tile
     ("bf16", 1024, 4096, 1536),   # several full 256x256 tiles
+    ("bf16", 512, 256, 1024),     # interior tiles only: 16-byte output stores
+    ("bf16", 512, 256, 516),      # rows of 516 columns are not 16-byte aligned: 8-byte stores everywhere
+    ("bf16", 8192, 128, 4096),    # 512 tiles: each workgroup of the resident grid walks two
+    ("bf16", 8200, 192, 4100),    # 561 tiles, ragged M and N, an odd number of k-tiles per tile
     ("bf16", 1, 4096, 6144),      # one token: weight-streaming kernel, whole 512-wide chunks
     ("bf16", 2, 1000, 260),       # K = 512 + 488: the last chunk is ragged
     ("bf16", 4, 14336, 512),      # four tokens, 28 chunks (two in flight per wave, one left over)
