@@ -233,6 +233,11 @@ SMALL_ROWS16 = wl.Workload(35, "small-gqa-8kv-b16", "bf16", 2048, 16, 8, 1536, 2
                            prefill_len=100, decode_steps=4, norm_gains=GAINS)
 RAGGED1 = wl.Workload(33, "ragged-640-b1", "bf16", 640, 5, 1, 1712, 8, None, 1e-5, 1e4, batch=1, prefill_len=45,
                       decode_steps=4, norm_gains=GAINS)
+# three tokens per decode step over 300-302 cached rows: the weight-streaming
+# projections, and decode attention in three splits whose partials live in the
+# workspace
+SPLIT3 = wl.Workload(37, "small-gqa-8kv-b3-split", "bf16", 2048, 16, 8, 1536, 256, 0.25, 1e-5, 5e5, batch=3,
+                     prefill_len=300, decode_steps=3, norm_gains=GAINS)
 # 40 tokens per decode step: 64-row tiles over 40 rows (a ragged row tail) with K split
 SMALL_ROWS40 = wl.Workload(36, "small-gqa-8kv-b40", "bf16", 2048, 16, 8, 1536, 256, 0.25, 1e-5, 5e5, batch=40,
                            prefill_len=100, decode_steps=3, norm_gains=GAINS)
@@ -267,10 +272,11 @@ def test_decode_chain_matches_prefill_and_oracle(w):
     check(chain, f64(full), "bf16", "chain vs full prefill (GPU vs GPU)")
 
 
-@pytest.mark.parametrize("w", [SMALL_ROWS6, SMALL_ROWS16, SMALL_ROWS40], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [SPLIT3, SMALL_ROWS6, SMALL_ROWS16, SMALL_ROWS40], ids=lambda w: w.name)
 def test_decode_step_ignores_workspace_contents(w):
-    """5-64 tokens: the projections split K through fp32 partial tiles in the
-    workspace (wo's reduction fused with ffn_norm).  Each decode step runs three
+    """1-4 tokens: the attention's split partials live in the workspace; 5-64
+    tokens: the projections split K through fp32 partial tiles in the workspace
+    (wo's reduction fused with ffn_norm).  Each decode step runs three
     times: over a workspace with every bit set, over a zeroed one, and over the
     previous call's leftovers; the outputs must agree bit for bit and follow the
     oracle's prefill + decode chain (40 rows: 64-row tiles with a ragged tail)."""
