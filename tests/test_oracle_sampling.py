@@ -39,6 +39,22 @@ def test_hand_computed_cut_and_draw():
     assert osm.sample_row(lg, 1.0, 0.81, 0.99) == 0
 
 
+def test_hand_computed_decision_margins():
+    # The GPU sampling tests compare a draw exactly only where this helper says
+    # the float32 arithmetic cannot flip it.  Same four tokens: mass before each
+    # in sorted order 0, 0.5, 0.8, 0.95.
+    lg = _logits_for([0.15, 0.5, 0.05, 0.3])
+    mp, mu = osm.decision_margins(lg, 1.0, 0.75, 0.6)
+    assert mp == pytest.approx(0.05, abs=1e-12)         # |0.8 - 0.75|
+    assert mu == pytest.approx(0.025, abs=1e-12)        # kept {1, 3}: cdf 0.625, 1; |0.625 - 0.6|
+    mp, mu = osm.decision_margins(lg, 1.0, 0.81, 0.9)
+    assert mp == pytest.approx(0.01, abs=1e-12)         # |0.8 - 0.81|
+    assert mu == pytest.approx(0.9 - 0.8 / 0.95, abs=1e-12)  # kept {1, 3, 0}: cdf .5/.95, .8/.95, 1
+    mp, mu = osm.decision_margins(lg, 1.0, 0.5, 0.5)    # exactly on the cut and on a boundary
+    assert mp == 0.0
+    assert mu == pytest.approx(0.125, abs=1e-12)        # the cut keeps {1, 3}: |0.625 - 0.5|
+
+
 def test_draw_induces_the_renormalised_kept_distribution():
     rng = np.random.default_rng(7)
     lg = rng.normal(0.0, 2.0, 50)
